@@ -1,0 +1,279 @@
+"""Python binding of libdecode_attn.so (the gfx950 decode-attention library).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind the C ABI declared in ``include/decode_attn.h``. PyTorch
+provides device memory and the stream; nothing here computes on its own, and
+there is no fallback -- if the library is missing or fails to load, every call
+raises.
+
+The names mirror the C entry points: ``decode_attn_fwd``, ``decode_attn_only``,
+``oproj_fwd``, ``gemm_f16``, ``decode_attn_workspace_size``,
+``oproj_workspace_size``, ``decode_attn_plan``, ``decode_attn_status_str``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdecode_attn.so")
+
+DA_OK = 0
+DA_ERR_NULL = -1
+DA_ERR_SHAPE = -2
+DA_ERR_ALIGN = -3
+DA_ERR_WORKSPACE = -4
+DA_ERR_LAUNCH = -5
+DA_HEAD_DIM = 128
+DA_MAX_GROUP = 16
+DA_FLAG_DEBUG_SCORES = 1
+
+EXPORTED = (
+    "decode_attn_workspace_size",
+    "decode_attn_plan",
+    "decode_attn_fwd",
+    "decode_attn_only",
+    "oproj_workspace_size",
+    "oproj_fwd",
+    "gemm_f16",
+    "decode_attn_status_str",
+)
+
+
+class DecodeAttnShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("flags", ctypes.c_uint32),
+        ("debug_scores", ctypes.c_void_p),
+        ("debug_lse", ctypes.c_void_p),
+    ]
+
+
+class MatmulPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("m", "k", "n", "tile_m", "tile_k", "tile_n", "split", "workgroups")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class DecodeAttnPlan(ctypes.Structure):
+    _fields_ = [
+        ("qk", MatmulPlan),
+        ("pv", MatmulPlan),
+        ("oproj", MatmulPlan),
+        ("split_len", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("oproj_path", ctypes.c_int32),
+        ("fused", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class DecodeAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_str(status), status))
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libdecode_attn.so not found at %s: build it first (python -c 'import "
+                           "__graft_entry__ as g; g.build()' or python decode_attention_output_amd/build.py)"
+                           % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    shp = ctypes.POINTER(DecodeAttnShape)
+    lib.decode_attn_workspace_size.restype = sz
+    lib.decode_attn_workspace_size.argtypes = [shp]
+    lib.decode_attn_plan.restype = ctypes.c_int
+    lib.decode_attn_plan.argtypes = [shp, ctypes.POINTER(DecodeAttnPlan)]
+    lib.decode_attn_fwd.restype = ctypes.c_int
+    lib.decode_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, shp, vp]
+    lib.decode_attn_only.restype = ctypes.c_int
+    lib.decode_attn_only.argtypes = [vp, vp, vp, vp, vp, shp, vp]
+    lib.oproj_workspace_size.restype = sz
+    lib.oproj_workspace_size.argtypes = [i32, i32, i32]
+    lib.oproj_fwd.restype = ctypes.c_int
+    lib.oproj_fwd.argtypes = [vp, vp, vp, i32, i32, i32, vp, sz, vp]
+    lib.gemm_f16.restype = ctypes.c_int
+    lib.gemm_f16.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    lib.decode_attn_status_str.restype = ctypes.c_char_p
+    lib.decode_attn_status_str.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().decode_attn_status_str(int(status)).decode()
+
+
+decode_attn_status_str = status_str
+
+
+def make_shape(batch, num_q_heads, num_kv_heads, max_seq_len, hidden=0, head_dim=DA_HEAD_DIM, softmax_scale=0.0,
+               workspace=None, workspace_bytes=0, flags=0, debug_scores=None, debug_lse=None) -> DecodeAttnShape:
+    return DecodeAttnShape(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(max_seq_len),
+                           int(hidden), float(softmax_scale), workspace, int(workspace_bytes), int(flags),
+                           debug_scores, debug_lse)
+
+
+def decode_attn_workspace_size(shape: DecodeAttnShape) -> int:
+    return int(load_library().decode_attn_workspace_size(ctypes.byref(shape)))
+
+
+def oproj_workspace_size(M: int, K: int, N: int) -> int:
+    return int(load_library().oproj_workspace_size(int(M), int(K), int(N)))
+
+
+def decode_attn_plan(shape: DecodeAttnShape) -> DecodeAttnPlan:
+    plan = DecodeAttnPlan()
+    rc = load_library().decode_attn_plan(ctypes.byref(shape), ctypes.byref(plan))
+    if rc != DA_OK:
+        raise DecodeAttnError(rc, "decode_attn_plan")
+    return plan
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers (torch supplies device buffers and the stream)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(name, t, dtype):
+    torch = _torch()
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return torch
+
+
+class Workspace:
+    """Zero-filled device scratch reused across calls (grows on demand)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device or "cuda")
+        return self.buf
+
+
+def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Optional[Workspace] = None,
+                    softmax_scale: float = 0.0, debug_scores=None, debug_lse=None, stream=None):
+    """One decode step: returns out [B, hidden] bf16."""
+    torch = _check_dev("q", q, _torch().bfloat16)
+    _check_dev("k_cache", k_cache, torch.bfloat16)
+    _check_dev("v_cache", v_cache, torch.bfloat16)
+    _check_dev("seq_lens", seq_lens, torch.int32)
+    _check_dev("o_weight", o_weight, torch.bfloat16)
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    hidden = o_weight.shape[1]
+    if out is None:
+        out = torch.empty((B, hidden), dtype=torch.bfloat16, device=q.device)
+    flags = DA_FLAG_DEBUG_SCORES if debug_scores is not None else 0
+    shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale, flags=flags, debug_scores=_ptr(debug_scores),
+                       debug_lse=_ptr(debug_lse))
+    need = decode_attn_workspace_size(shape)
+    ws = (workspace or Workspace(q.device)).get(need)
+    shape.workspace = _ptr(ws)
+    shape.workspace_bytes = 0 if ws is None else ws.numel()
+    rc = load_library().decode_attn_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                        o_weight.data_ptr(), out.data_ptr(), ctypes.byref(shape),
+                                        _stream_handle(stream))
+    if rc != DA_OK:
+        raise DecodeAttnError(rc, "decode_attn_fwd")
+    return out
+
+
+def decode_attn_only(q, k_cache, v_cache, seq_lens, out=None, workspace: Optional[Workspace] = None,
+                     softmax_scale: float = 0.0, debug_scores=None, debug_lse=None, stream=None):
+    """Attention only: returns the bf16 [B, Hq*D] head-major attention output."""
+    torch = _check_dev("q", q, _torch().bfloat16)
+    _check_dev("k_cache", k_cache, torch.bfloat16)
+    _check_dev("v_cache", v_cache, torch.bfloat16)
+    _check_dev("seq_lens", seq_lens, torch.int32)
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((B, Hq * D), dtype=torch.bfloat16, device=q.device)
+    flags = DA_FLAG_DEBUG_SCORES if debug_scores is not None else 0
+    shape = make_shape(B, Hq, Hkv, Lmax, 8, D, softmax_scale, flags=flags, debug_scores=_ptr(debug_scores),
+                       debug_lse=_ptr(debug_lse))
+    need = decode_attn_workspace_size(shape)
+    ws = (workspace or Workspace(q.device)).get(need)
+    shape.workspace = _ptr(ws)
+    shape.workspace_bytes = 0 if ws is None else ws.numel()
+    rc = load_library().decode_attn_only(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                         out.data_ptr(), ctypes.byref(shape), _stream_handle(stream))
+    if rc != DA_OK:
+        raise DecodeAttnError(rc, "decode_attn_only")
+    return out
+
+
+def oproj_fwd(x, w, out=None, workspace: Optional[Workspace] = None, stream=None):
+    """out [M, N] = x [M, K] @ w [K, N], bf16."""
+    torch = _check_dev("x", x, _torch().bfloat16)
+    _check_dev("w", w, torch.bfloat16)
+    M, K = x.shape
+    N = w.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    need = oproj_workspace_size(M, K, N)
+    ws = (workspace or Workspace(x.device)).get(need)
+    rc = load_library().oproj_fwd(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, K, N, _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream_handle(stream))
+    if rc != DA_OK:
+        raise DecodeAttnError(rc, "oproj_fwd")
+    return out
+
+
+def gemm_f16(a, b, c=None, stream=None):
+    """C [M, N] = A [M, K] @ B [K, N], fp16."""
+    torch = _check_dev("a", a, _torch().float16)
+    _check_dev("b", b, torch.float16)
+    M, K = a.shape
+    N = b.shape[1]
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    rc = load_library().gemm_f16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, _stream_handle(stream))
+    if rc != DA_OK:
+        raise DecodeAttnError(rc, "gemm_f16")
+    return c

@@ -1,0 +1,360 @@
+// C ABI of the library: argument checks, per-matmul tile selection, workspace
+// layout and the launch sequence of one decode step.
+//
+// Tile selection follows the per-matmul lesson of "PyPTO 开箱性能调优实战：
+// Decode Attention 多 Matmul 独立 TileShape 配置 F-16" (sections 核心原则 and
+// 迭代过程): every matmul of the step gets a tile sized to its own M/K/N --
+// a tiny M (the query group, the batch) is never padded past one 16-row
+// operand, a short axis (head_dim 128) is not split, and a long axis (the
+// keys, the projection's K and N) is cut into many large slices so that the
+// 256 compute units each receive several workgroups.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/decode_attn.h"
+#include "gfx950.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+using da::kHeadDim;
+
+constexpr int kAttnWorkgroups = 512;        // stream-K attention: two per compute unit
+constexpr int kAttnBlockKeys = 32;          // keys per wave step
+constexpr int kTargetProjWorkgroups = 256;   // one per compute unit
+constexpr int kGemvUnroll = 8;               // weight rows per lane in flight
+constexpr int kGemmKStep = 128;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
+
+bool shape_ok(const decode_attn_shape_t* s, bool need_hidden) {
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->max_seq_len < 1) return false;
+  if (s->head_dim != kHeadDim) return false;
+  if (s->num_q_heads % s->num_kv_heads != 0) return false;
+  if (s->num_q_heads / s->num_kv_heads > DA_MAX_GROUP) return false;
+  if (need_hidden && (s->hidden < 1 || s->hidden % 8 != 0)) return false;
+  if (s->batch > da::kMaxAttnBatch) return false;
+  if (s->max_seq_len > (1 << 24)) return false;  // one sequence's K rows stay below 4 GiB
+  // element counts must stay addressable
+  const double kv = (double)s->batch * s->num_kv_heads * s->max_seq_len * kHeadDim;
+  if (kv > 9.0e15) return false;
+  return true;
+}
+
+// ---- projection tiles (shared by decode_attn_fwd and oproj_fwd) ----
+struct ProjPlan {
+  int path;  // 0 GEMV, 1 MFMA
+  int mpad;  // GEMV rows held per lane (power of two >= M)
+  int tile_n;  // output columns per workgroup
+  int kchunk, ksplit;
+  int tiles;  // output tiles (counters)
+  size_t part_bytes;
+};
+
+ProjPlan plan_proj(int M, int K, int N) {
+  ProjPlan pp{};
+  if (M < 16) {
+    // GEMV: the widest column tile the accumulators allow (a wave then reads
+    // whole KiB-long row pieces), never much wider than N itself; the K axis
+    // is cut so that about kTargetProjWorkgroups workgroups stream the weight.
+    pp.path = 0;
+    pp.mpad = pow2_at_least(M);
+    int tc = pp.mpad <= 4 ? 512 : (pp.mpad <= 8 ? 256 : 128);
+    while (tc > 64 && tc / 2 >= N) tc /= 2;
+    pp.tile_n = tc;
+    pp.tiles = ceil_div(N, tc);
+    const int gran = (2048 / tc) * kGemvUnroll;  // rows one pass of the workgroup covers
+    int ksplit = std::max(1, kTargetProjWorkgroups / pp.tiles);
+    ksplit = std::min(ksplit, std::max(1, ceil_div(K, gran)));
+    int kchunk = (int)align_up((size_t)ceil_div(K, ksplit), gran);
+    const int max_chunk = 32768 / (4 * pp.mpad);  // activations of a chunk fit 32 KiB of LDS
+    kchunk = std::min(kchunk, std::max(gran, max_chunk / gran * gran));
+    pp.kchunk = kchunk;
+    pp.ksplit = ceil_div(K, kchunk);
+  } else {
+    pp.path = 1;
+    pp.mpad = 16;
+    pp.tile_n = 64;
+    pp.tiles = ceil_div(N, 64) * ceil_div(M, 16);
+    int ksplit = std::max(1, kTargetProjWorkgroups / pp.tiles);
+    ksplit = std::min(ksplit, std::max(1, K / kGemmKStep));
+    pp.kchunk = (int)align_up((size_t)ceil_div(K, ksplit), kGemmKStep);
+    pp.ksplit = ceil_div(K, pp.kchunk);
+  }
+  if (pp.ksplit > 1) pp.part_bytes = align_up((size_t)pp.ksplit * M * N * sizeof(float), kAlign);
+  return pp;
+}
+
+// ---- attention: stream-K over the keys of all sequences ----
+struct AttnPlan {
+  int gpad;
+  int workgroups;  // stream-K workgroups
+  int keys_per_wg; // upper bound of the keys one workgroup streams
+  size_t slots;
+  size_t part_o_bytes, part_ml_bytes;
+};
+
+AttnPlan plan_attn(const decode_attn_shape_t* s) {
+  AttnPlan ap{};
+  const int G = s->num_q_heads / s->num_kv_heads;
+  ap.gpad = pow2_at_least(G);
+  const long pairs = (long)s->batch * s->num_kv_heads;
+  const long blocks_max = pairs * ceil_div(s->max_seq_len, kAttnBlockKeys);
+  ap.workgroups = (int)std::min<long>(kAttnWorkgroups, blocks_max);
+  ap.keys_per_wg = ceil_div(blocks_max, ap.workgroups) * kAttnBlockKeys;
+  ap.slots = (size_t)ap.workgroups + (size_t)pairs;
+  ap.part_o_bytes = align_up(ap.slots * G * kHeadDim * sizeof(float), kAlign);
+  ap.part_ml_bytes = align_up(ap.slots * G * 2 * sizeof(float), kAlign);
+  return ap;
+}
+
+struct Layout {
+  AttnPlan attn;
+  ProjPlan proj;
+  size_t off_part_o, off_part_ml, off_flat, off_proj_part, total;
+  int attn_counter0, proj_counter0;
+  bool fits;
+};
+
+// Workspace: [arrival counters][attention partials][attention output][projection partials]
+Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
+  Layout L{};
+  L.attn = plan_attn(s);
+  size_t off = da::kCounterBlockBytes;
+  L.off_part_o = off;
+  off += L.attn.part_o_bytes;
+  L.off_part_ml = off;
+  off += L.attn.part_ml_bytes;
+  L.attn_counter0 = 0;
+  int counters = s->batch * s->num_kv_heads;
+  if (with_proj) {
+    L.proj = plan_proj(s->batch, s->num_q_heads * kHeadDim, s->hidden);
+    L.off_flat = off;
+    off += align_up((size_t)s->batch * s->num_q_heads * kHeadDim * sizeof(uint16_t), kAlign);
+    L.off_proj_part = off;
+    off += L.proj.part_bytes;
+    L.proj_counter0 = counters;
+    counters += L.proj.tiles;
+  }
+  L.total = off;
+  L.fits = counters <= da::kMaxCounters && L.attn.part_o_bytes < (1ull << 32);
+  return L;
+}
+
+int check_attn_ptrs(const void* q, const void* k, const void* v, const int32_t* sl, const void* out) {
+  if (!q || !k || !v || !sl || !out) return DA_ERR_NULL;
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) || misaligned(sl, 4))
+    return DA_ERR_ALIGN;
+  return DA_OK;
+}
+
+int check_workspace(const decode_attn_shape_t* s, size_t need) {
+  if (need == 0) return DA_OK;
+  if (!s->workspace || s->workspace_bytes < need) return DA_ERR_WORKSPACE;
+  if (misaligned(s->workspace, kAlign)) return DA_ERR_ALIGN;
+  return DA_OK;
+}
+
+int check_debug(const decode_attn_shape_t* s) {
+  if (!(s->flags & DA_FLAG_DEBUG_SCORES)) return DA_OK;
+  if (!s->debug_scores || !s->debug_lse) return DA_ERR_NULL;
+  if (misaligned(s->debug_scores, 4) || misaligned(s->debug_lse, 4)) return DA_ERR_ALIGN;
+  return DA_OK;
+}
+
+da::AttnParams attn_params(const void* q, const void* k, const void* v, const int32_t* sl, void* flat,
+                           const decode_attn_shape_t* s, const Layout& L) {
+  da::AttnParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.seq_lens = sl;
+  p.flat = (uint16_t*)flat;
+  char* ws = (char*)s->workspace;
+  p.part_o = (float*)(ws + L.off_part_o);
+  p.part_ml = (float*)(ws + L.off_part_ml);
+  p.part_o_bytes = (uint32_t)L.attn.part_o_bytes;
+  p.part_ml_bytes = (uint32_t)L.attn.part_ml_bytes;
+  p.counters = (uint32_t*)ws + L.attn_counter0;
+  const bool dbg = (s->flags & DA_FLAG_DEBUG_SCORES) != 0;
+  p.dbg_scores = dbg ? s->debug_scores : nullptr;
+  p.dbg_lse = dbg ? s->debug_lse : nullptr;
+  p.B = s->batch;
+  p.Hq = s->num_q_heads;
+  p.Hkv = s->num_kv_heads;
+  p.G = s->num_q_heads / s->num_kv_heads;
+  p.Lmax = s->max_seq_len;
+  p.num_workgroups = L.attn.workgroups;
+  const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return p;
+}
+
+int run_attention(const da::AttnParams& p, const Layout& L, hipStream_t st) {
+  return da::launch_attention(p, L.attn.gpad, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+int run_proj(const ProjPlan& pp, const void* x, const void* w, void* out, int M, int K, int N, char* part,
+             char* cnt, hipStream_t st) {
+  if (pp.path == 0) {
+    da::GemvParams g{};
+    g.x = (const uint16_t*)x;
+    g.w = (const uint16_t*)w;
+    g.out = (uint16_t*)out;
+    g.part = (float*)part;
+    g.counters = (uint32_t*)cnt;
+    g.M = M;
+    g.K = K;
+    g.N = N;
+    g.kchunk = pp.kchunk;
+    g.ksplit = pp.ksplit;
+    g.tile_n = pp.tile_n;
+    return da::launch_gemv(g, pp.mpad, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+  }
+  da::GemmParams g{};
+  g.a = (const uint16_t*)x;
+  g.b = (const uint16_t*)w;
+  g.c = (uint16_t*)out;
+  g.part = (float*)part;
+  g.counters = (uint32_t*)cnt;
+  g.M = M;
+  g.K = K;
+  g.N = N;
+  g.kchunk = pp.kchunk;
+  g.ksplit = pp.ksplit;
+  return da::launch_gemm_bf16(g, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t decode_attn_workspace_size(const decode_attn_shape_t* shape) {
+  if (!shape || !shape_ok(shape, true)) return 0;
+  const Layout L = layout_for(shape, true);
+  return L.fits ? L.total : 0;
+}
+
+int decode_attn_plan(const decode_attn_shape_t* shape, decode_attn_plan_t* plan) {
+  if (!shape || !plan) return DA_ERR_NULL;
+  if (!shape_ok(shape, true)) return DA_ERR_SHAPE;
+  const Layout L = layout_for(shape, true);
+  if (!L.fits) return DA_ERR_SHAPE;
+  const int G = shape->num_q_heads / shape->num_kv_heads;
+  const int Ko = shape->num_q_heads * kHeadDim;
+  memset(plan, 0, sizeof *plan);
+  const int wgs = L.attn.workgroups;
+  // QK^T per kv head: M = G, K = head_dim (whole), N = keys (32 per wave step)
+  plan->qk = {G, kHeadDim, shape->max_seq_len, 16, kHeadDim, kAttnBlockKeys, wgs, wgs};
+  // attn x V per kv head: M = G, K = keys (32 per wave step), N = head_dim (whole)
+  plan->pv = {G, shape->max_seq_len, kHeadDim, L.attn.gpad, kAttnBlockKeys, kHeadDim, wgs, wgs};
+  plan->oproj = {shape->batch, Ko, shape->hidden, L.proj.mpad, L.proj.kchunk, L.proj.tile_n, L.proj.ksplit,
+                 L.proj.tiles * L.proj.ksplit};
+  plan->split_len = L.attn.keys_per_wg;
+  plan->num_splits = wgs;
+  plan->oproj_path = L.proj.path;
+  plan->fused = 0;
+  plan->workspace_bytes = L.total;
+  return DA_OK;
+}
+
+int decode_attn_fwd(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                    const void* o_weight, void* out, const decode_attn_shape_t* shape, void* stream) {
+  if (!shape) return DA_ERR_NULL;
+  int rc = check_attn_ptrs(q, k_cache, v_cache, seq_lens, out);
+  if (rc) return rc;
+  if (!o_weight) return DA_ERR_NULL;
+  if (misaligned(o_weight, 16)) return DA_ERR_ALIGN;
+  if (!shape_ok(shape, true)) return DA_ERR_SHAPE;
+  const Layout L = layout_for(shape, true);
+  if (!L.fits) return DA_ERR_SHAPE;
+  if ((rc = check_workspace(shape, L.total))) return rc;
+  if ((rc = check_debug(shape))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)shape->workspace;
+  void* flat = ws + L.off_flat;
+  const da::AttnParams p = attn_params(q, k_cache, v_cache, seq_lens, flat, shape, L);
+  if ((rc = run_attention(p, L, st))) return rc;
+  return run_proj(L.proj, flat, o_weight, out, shape->batch, shape->num_q_heads * kHeadDim, shape->hidden,
+                  ws + L.off_proj_part, (char*)((uint32_t*)ws + L.proj_counter0), st);
+}
+
+int decode_attn_only(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                     void* attn_out, const decode_attn_shape_t* shape, void* stream) {
+  if (!shape) return DA_ERR_NULL;
+  int rc = check_attn_ptrs(q, k_cache, v_cache, seq_lens, attn_out);
+  if (rc) return rc;
+  if (!shape_ok(shape, false)) return DA_ERR_SHAPE;
+  const Layout L = layout_for(shape, false);
+  if (!L.fits) return DA_ERR_SHAPE;
+  if ((rc = check_workspace(shape, L.total))) return rc;
+  if ((rc = check_debug(shape))) return rc;
+  const da::AttnParams p = attn_params(q, k_cache, v_cache, seq_lens, attn_out, shape, L);
+  return run_attention(p, L, (hipStream_t)stream);
+}
+
+size_t oproj_workspace_size(int32_t M, int32_t K, int32_t N) {
+  if (M < 1 || K < 1 || N < 1) return 0;
+  const ProjPlan pp = plan_proj(M, K, N);
+  if (pp.tiles > da::kMaxCounters) return 0;
+  return pp.ksplit > 1 ? da::kCounterBlockBytes + pp.part_bytes : 0;
+}
+
+int oproj_fwd(const void* x, const void* w, void* out, int32_t M, int32_t K, int32_t N, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (!x || !w || !out) return DA_ERR_NULL;
+  if (misaligned(x, 16) || misaligned(w, 16) || misaligned(out, 16)) return DA_ERR_ALIGN;
+  if (M < 1 || K < 1 || N < 1 || N % 8 != 0) return DA_ERR_SHAPE;
+  if (M >= 16 && K % 32 != 0) return DA_ERR_SHAPE;
+  if (M < 16 && K % 8 != 0) return DA_ERR_SHAPE;
+  const ProjPlan pp = plan_proj(M, K, N);
+  if (pp.tiles > da::kMaxCounters) return DA_ERR_SHAPE;
+  const size_t need = oproj_workspace_size(M, K, N);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return DA_ERR_WORKSPACE;
+    if (misaligned(workspace, kAlign)) return DA_ERR_ALIGN;
+  }
+  char* ws = (char*)workspace;
+  return run_proj(pp, x, w, out, M, K, N, ws ? ws + da::kCounterBlockBytes : nullptr, ws, (hipStream_t)stream);
+}
+
+int gemm_f16(const void* a, const void* b, void* c, int32_t M, int32_t N, int32_t K, void* stream) {
+  if (!a || !b || !c) return DA_ERR_NULL;
+  if (misaligned(a, 16) || misaligned(b, 16) || misaligned(c, 16)) return DA_ERR_ALIGN;
+  if (M < 1 || N < 1 || K < 1 || M % 16 != 0 || N % 16 != 0 || K % 32 != 0) return DA_ERR_SHAPE;
+  da::GemmParams g{};
+  g.a = (const uint16_t*)a;
+  g.b = (const uint16_t*)b;
+  g.c = (uint16_t*)c;
+  g.M = M;
+  g.K = K;
+  g.N = N;
+  g.kchunk = (int)align_up((size_t)K, kGemmKStep);
+  g.ksplit = 1;
+  return da::launch_gemm_f16(g, (hipStream_t)stream) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+const char* decode_attn_status_str(int status) {
+  switch (status) {
+    case DA_OK: return "ok";
+    case DA_ERR_NULL: return "a required pointer is NULL";
+    case DA_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case DA_ERR_ALIGN: return "misaligned pointer (16-byte tensors, 256-byte workspace)";
+    case DA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+/*
+ * decode_attn.h -- C ABI of the MI355X (gfx950) decode-attention library.
+ *
+ * One grouped-query decode-attention step followed by the output projection,
+ * as in "PyPTO 开箱性能调优实战：Decode Attention 多 Matmul 独立 TileShape
+ * 配置 F-16" (section 代码对比; shapes in the table of section 三个 Matmul 的
+ * Shape 特征分析):
+ *
+ *   scores[g, j] = (q[b, h*G+g, :] . K[b, h, j, :]) * softmax_scale   fp32
+ *   p[g, :]      = softmax over j < seq_lens[b] of scores[g, :]
+ *   o[b, h*G+g]  = sum_j p[g, j] * V[b, h, j, :]                      -> bf16
+ *   out[b, :]    = flat(o)[b, :] @ o_weight                            -> bf16
+ *
+ * with G = num_q_heads / num_kv_heads, flat(o) head-major (column qh*D + d)
+ * and o_weight [num_q_heads*head_dim, hidden] row-major (no transpose).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named *_dev are device pointers (hipMalloc or equivalent). The
+ *    caller owns every buffer; the library never allocates or frees memory
+ *    and keeps no pointer after it returns.
+ *  - 16-bit tensors are raw bf16 (or fp16 where stated) words, densely packed
+ *    in the row-major layout given, every base address 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is only enqueued; the outputs are valid once the stream has
+ *    reached that point. Nothing blocks the host.
+ *  - Every argument check happens before any HIP call, so a non-zero status
+ *    means nothing was enqueued (except DA_ERR_LAUNCH, reported after a
+ *    launch failed).
+ *  - Calls that share a workspace must be ordered (same stream or
+ *    synchronised); calls with distinct workspaces may run concurrently.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define DA_OK 0
+#define DA_ERR_NULL (-1)      /* a required pointer is NULL                          */
+#define DA_ERR_SHAPE (-2)     /* unsupported or inconsistent sizes                    */
+#define DA_ERR_ALIGN (-3)     /* a base address is not 16-byte aligned                */
+#define DA_ERR_WORKSPACE (-4) /* workspace missing or smaller than required          */
+#define DA_ERR_LAUNCH (-5)    /* a kernel launch failed (hipGetLastError after it)   */
+
+/* Only head_dim 128 is implemented. */
+#define DA_HEAD_DIM 128
+/* Largest query-head group (num_q_heads / num_kv_heads). */
+#define DA_MAX_GROUP 16
+
+/* flags */
+#define DA_FLAG_DEBUG_SCORES 1u /* also write debug_scores / debug_lse (test use) */
+
+/*
+ * Shape and per-call options of one decode step. All sizes in elements.
+ *
+ *  batch          B >= 1
+ *  num_q_heads    Hq >= 1, a multiple of num_kv_heads, Hq/Hkv <= DA_MAX_GROUP
+ *  num_kv_heads   Hkv >= 1
+ *  head_dim       D, must be DA_HEAD_DIM
+ *  max_seq_len    Lmax >= 1: rows per (batch, kv head) in the K/V caches
+ *  hidden         N >= 1, output features of the projection (its K is Hq*D);
+ *                 unused by decode_attn_only
+ *  softmax_scale  multiplier of q.k; 0 selects 1/sqrt(head_dim)
+ *  workspace      device scratch of at least decode_attn_workspace_size()
+ *                 bytes, 256-byte aligned. It must be zero-filled before its
+ *                 first use; every completed call leaves it ready for the
+ *                 next one (its counters return to zero).
+ *  workspace_bytes size of that buffer
+ *  flags          DA_FLAG_* bits
+ *  debug_scores   with DA_FLAG_DEBUG_SCORES: device fp32 [B, Hq, Lmax]; entry
+ *                 [b, qh, j] receives the scaled score of key j for j <
+ *                 seq_lens[b]; other entries are left untouched
+ *  debug_lse      with DA_FLAG_DEBUG_SCORES: device fp32 [B, Hq], natural log
+ *                 of sum_j exp(score_j)
+ */
+typedef struct {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_seq_len;
+  int32_t hidden;
+  float softmax_scale;
+  void* workspace;
+  size_t workspace_bytes;
+  uint32_t flags;
+  float* debug_scores;
+  float* debug_lse;
+} decode_attn_shape_t;
+
+/*
+ * Tiles chosen for one shape: one entry per matmul of the step, each sized to
+ * its own M/K/N rather than one shared setting (the per-matmul tile lesson of
+ * the F-16 page, sections 核心原则 and 迭代过程). Filled by decode_attn_plan.
+ */
+typedef struct {
+  int32_t m, k, n;     /* the matmul's own M, K, N (per kv head / per step)           */
+  int32_t tile_m;      /* rows of M one wave holds (a 16-row MFMA operand, G valid)  */
+  int32_t tile_k;      /* K extent staged per step                                    */
+  int32_t tile_n;      /* N extent one workgroup owns                                 */
+  int32_t split;       /* number of independent slices along the reduced axis        */
+  int32_t workgroups;  /* workgroups launched for this matmul                          */
+} decode_attn_matmul_plan_t;
+
+typedef struct {
+  decode_attn_matmul_plan_t qk;     /* q_grouped x k_cache^T: M=G, K=D, N=keys       */
+  decode_attn_matmul_plan_t pv;     /* attn_weights x v_cache: M=G, K=keys, N=D      */
+  decode_attn_matmul_plan_t oproj;  /* attn_output_flat x o_weight: M=B, K=Hq*D, N   */
+  int32_t split_len;    /* keys per attention workgroup (flash-decoding split)       */
+  int32_t num_splits;   /* ceil(max_seq_len / split_len)                              */
+  int32_t oproj_path;   /* 0: VALU GEMV (B < 16), 1: MFMA GEMM (B >= 16)             */
+  int32_t fused;        /* 1: the whole step runs as one cooperative launch           */
+  size_t workspace_bytes;
+} decode_attn_plan_t;
+
+/* Bytes of workspace decode_attn_fwd / decode_attn_only need for `shape`
+ * (workspace fields ignored); 0 if the shape is invalid. */
+size_t decode_attn_workspace_size(const decode_attn_shape_t* shape);
+
+/* Host-only: fill `plan` with the tile choice for `shape`. No HIP call. */
+int decode_attn_plan(const decode_attn_shape_t* shape, decode_attn_plan_t* plan);
+
+/*
+ * The whole step.
+ *  q_dev         bf16 [B, Hq, D]
+ *  k_cache_dev   bf16 [B, Hkv, Lmax, D]   (rows >= seq_lens[b] are never read)
+ *  v_cache_dev   bf16 [B, Hkv, Lmax, D]
+ *  seq_lens_dev  int32 [B], each in [1, Lmax] (precondition, not checked on
+ *                the device; a value outside it gives undefined results)
+ *  o_weight_dev  bf16 [Hq*D, hidden]
+ *  out_dev       bf16 [B, hidden]
+ * Returns DA_OK or a DA_ERR_* code.
+ */
+int decode_attn_fwd(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                    const int32_t* seq_lens_dev, const void* o_weight_dev, void* out_dev,
+                    const decode_attn_shape_t* shape, void* stream);
+
+/* The first two matmuls and the softmax only: attn_out_dev receives the
+ * bf16 [B, Hq*D] head-major attention output (attn_output_flat). */
+int decode_attn_only(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                     const int32_t* seq_lens_dev, void* attn_out_dev, const decode_attn_shape_t* shape,
+                     void* stream);
+
+/* Bytes of workspace oproj_fwd needs for an [M,K] x [K,N] product. */
+size_t oproj_workspace_size(int32_t M, int32_t K, int32_t N);
+
+/*
+ * The output projection alone (the third matmul of the F-16 page):
+ * out[M,N] = x[M,K] @ w[K,N]; bf16 in, fp32 accumulation, bf16 out (round to
+ * nearest even). M < 16 runs a VALU GEMV, M >= 16 an MFMA GEMM. `workspace`
+ * (>= oproj_workspace_size bytes, zero-filled before first use, may be NULL
+ * when that size is 0) holds split-K partial sums and counters.
+ */
+int oproj_fwd(const void* x_dev, const void* w_dev, void* out_dev, int32_t M, int32_t K, int32_t N,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dense GEMM of the CANN msKPP BasicMatmul example ("自动调优流程 / Kernel级
+ * 自动调优"): C[M,N] = A[M,K] @ B[K,N], all fp16 row-major, fp32 accumulation,
+ * fp16 out (round to nearest even). M, N multiples of 16; K a multiple of 32.
+ */
+int gemm_f16(const void* a_dev, const void* b_dev, void* c_dev, int32_t M, int32_t N, int32_t K, void* stream);
+
+/* Static text for a status code. */
+const char* decode_attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

@@ -91,11 +91,15 @@ class OracleError(RuntimeError):
     pass
 
 
+MAX_THREADS = 16  # a fair share of a shared host
+
+
 def default_threads() -> int:
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    return max(1, min(n, MAX_THREADS))
 
 
 def _u16(a: np.ndarray) -> np.ndarray:

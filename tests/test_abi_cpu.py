@@ -1,0 +1,151 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, rejects bad arguments before touching the device, and plans one tile
+per matmul of the step."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_output_amd as da
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decode_attn.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "for", "sizeof")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(da.LIB_PATH):
+        from decode_attention_output_amd import build
+        build.build()
+    return da.load_library()
+
+
+def test_header_declares_the_binding_names():
+    assert _declared_functions() == sorted(da.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings(lib):
+    for code in (da.DA_OK, da.DA_ERR_NULL, da.DA_ERR_SHAPE, da.DA_ERR_ALIGN, da.DA_ERR_WORKSPACE, da.DA_ERR_LAUNCH):
+        assert da.status_str(code) and da.status_str(code) != "unknown status"
+    assert da.status_str(-99) == "unknown status"
+
+
+FAKE = 0x10000  # 16- and 256-byte aligned, never dereferenced: every call below fails its checks first
+
+
+def _shape(**kw):
+    base = dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=2048, hidden=4096)
+    base.update(kw)
+    return da.make_shape(**base)
+
+
+def _fwd(lib, shape, q=FAKE, k=FAKE, v=FAKE, sl=FAKE, w=FAKE, out=FAKE):
+    return lib.decode_attn_fwd(q, k, v, sl, w, out, ctypes.byref(shape), None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "sl", "w", "out"])
+def test_null_pointers_are_rejected(lib, which):
+    assert _fwd(lib, _shape(), **{which: None}) == da.DA_ERR_NULL
+    assert lib.decode_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == da.DA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim=64), dict(num_q_heads=30), dict(num_q_heads=8 * 17),
+                                dict(batch=0), dict(max_seq_len=0), dict(hidden=0), dict(hidden=4100),
+                                dict(num_kv_heads=0)])
+def test_bad_shapes_are_rejected(lib, kw):
+    s = _shape(**kw)
+    assert _fwd(lib, s) == da.DA_ERR_SHAPE
+    assert da.decode_attn_workspace_size(s) == 0
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "w", "out"])
+def test_misaligned_pointers_are_rejected(lib, which):
+    assert _fwd(lib, _shape(), **{which: FAKE + 2}) == da.DA_ERR_ALIGN
+
+
+def test_workspace_is_required_and_checked(lib):
+    s = _shape()
+    need = da.decode_attn_workspace_size(s)
+    assert need > 0
+    assert _fwd(lib, s) == da.DA_ERR_WORKSPACE
+    s.workspace, s.workspace_bytes = FAKE, need - 1
+    assert _fwd(lib, s) == da.DA_ERR_WORKSPACE
+    s.workspace, s.workspace_bytes = FAKE + 16, need
+    assert _fwd(lib, s) == da.DA_ERR_ALIGN
+
+
+def test_debug_pointers_required_with_the_flag(lib):
+    s = _shape(flags=da.DA_FLAG_DEBUG_SCORES)
+    s.workspace, s.workspace_bytes = FAKE, da.decode_attn_workspace_size(s)
+    assert _fwd(lib, s) == da.DA_ERR_NULL
+
+
+def test_oproj_and_gemm_argument_checks(lib):
+    assert lib.oproj_fwd(None, FAKE, FAKE, 1, 4096, 4096, FAKE, 1 << 30, None) == da.DA_ERR_NULL
+    assert lib.oproj_fwd(FAKE, FAKE, FAKE, 1, 4096, 4100, FAKE, 1 << 30, None) == da.DA_ERR_SHAPE
+    assert lib.oproj_fwd(FAKE, FAKE, FAKE + 8, 1, 4096, 4096, FAKE, 1 << 30, None) == da.DA_ERR_ALIGN
+    need = da.oproj_workspace_size(1, 4096, 4096)
+    assert need > 0
+    assert lib.oproj_fwd(FAKE, FAKE, FAKE, 1, 4096, 4096, FAKE, need - 1, None) == da.DA_ERR_WORKSPACE
+    assert lib.oproj_fwd(FAKE, FAKE, FAKE, 16, 4100, 4096, FAKE, 1 << 30, None) == da.DA_ERR_SHAPE
+    assert lib.gemm_f16(FAKE, None, FAKE, 256, 512, 1024, None) == da.DA_ERR_NULL
+    assert lib.gemm_f16(FAKE, FAKE, FAKE, 250, 512, 1024, None) == da.DA_ERR_SHAPE
+    assert lib.gemm_f16(FAKE, FAKE, FAKE, 256, 512, 1000, None) == da.DA_ERR_SHAPE
+
+
+def _golden_shapes():
+    rows = {}
+    for line in open(os.path.join(GOLDEN, "decode_attention_matmul_shapes.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            name, m, k, n = line.split()
+            rows[name] = (int(m), int(k), int(n))
+    return rows
+
+
+def test_plan_reports_the_pages_matmul_shapes(lib):
+    g = _golden_shapes()
+    plan = da.decode_attn_plan(_shape())
+    assert (plan.qk.m, plan.qk.k, plan.qk.n) == g["qk_t"]
+    assert (plan.pv.m, plan.pv.k, plan.pv.n) == g["attn_v"]
+    assert (plan.oproj.m, plan.oproj.k, plan.oproj.n) == g["output_proj"]
+
+
+@pytest.mark.parametrize("cfg", [dict(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=256, hidden=512),
+                                 dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=2048, hidden=4096),
+                                 dict(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=8192, hidden=4096),
+                                 dict(batch=4, num_q_heads=64, num_kv_heads=8, max_seq_len=32768, hidden=8192)])
+def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
+    plan = da.decode_attn_plan(da.make_shape(**cfg))
+    G = cfg["num_q_heads"] // cfg["num_kv_heads"]
+    # a short axis is not split: head_dim 128 stays whole in QK^T (its K) and PV (its N)
+    assert plan.qk.tile_k == 128 and plan.pv.tile_n == 128
+    # the tiny M (query group) sits in one 16-row operand and is not padded further
+    assert plan.qk.tile_m == 16 and G <= plan.pv.tile_m <= 16
+    # the long axis (keys) is streamed 32 keys per wave step and cut evenly over the workgroups
+    assert plan.qk.tile_n == 32 and plan.pv.tile_k == 32
+    keys = cfg["batch"] * cfg["num_kv_heads"] * cfg["max_seq_len"]
+    assert plan.split_len % 32 == 0 and plan.split_len * plan.num_splits >= keys
+    assert plan.split_len * (plan.num_splits - 1) < keys + 32 * plan.num_splits
+    # every matmul gets enough workgroups to occupy the 256 compute units when the problem allows it
+    if keys >= 256 * 32:
+        assert plan.qk.workgroups >= 256
+    assert plan.oproj.workgroups >= min(256, (cfg["hidden"] // 64) * (cfg["num_q_heads"] * 128 // 256))
+    # projection path: VALU GEMV below 16 rows, MFMA from 16 rows
+    assert plan.oproj_path == (1 if cfg["batch"] >= 16 else 0)
+    assert plan.workspace_bytes == da.decode_attn_workspace_size(da.make_shape(**cfg))

@@ -1,0 +1,224 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every case draws seeded inputs, runs the library on the GPU and the oracle on
+the host, and compares element by element:
+  * bf16 outputs: max |gpu - ref| <= 1e-2 and max relative error <= 2^-7 where
+    |ref| >= 1e-2 (ref = the oracle's unrounded double result);
+  * fp32 debug scores: |gpu - ref| <= 1e-4 * max(|ref|, 1);
+  * integer-valued GEMMs and the closed-form special cases: bit-exact.
+The four decode workloads run at their full sizes in the same launch
+configuration the benchmark times (the library picks it from the shape).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_output_amd as da
+import oracle
+import workloads
+from gpu_helpers import (assert_bf16_close, assert_scores_close, assert_within_fp32_sum_bound, bf16_words_to_f64,
+                         dev_bf16, dev_f16, dev_i32, host_words)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_step(inp, ws=None, scale=0.0, debug=False):
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    sl, w = dev_i32(inp["seq_lens"]), dev_bf16(inp["o_weight"])
+    ws = ws or da.Workspace()
+    flat = da.decode_attn_only(q, k, v, sl, workspace=ws, softmax_scale=scale)
+    out = da.decode_attn_fwd(q, k, v, sl, w, workspace=ws, softmax_scale=scale)
+    res = {"flat": host_words(flat), "out": host_words(out)}
+    if debug:
+        B, Hq, _ = inp["q"].shape
+        Lmax = inp["k"].shape[2]
+        dbg_s = torch.full((B, Hq, Lmax), float("nan"), dtype=torch.float32, device="cuda")
+        dbg_l = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+        da.decode_attn_only(q, k, v, sl, workspace=ws, softmax_scale=scale, debug_scores=dbg_s, debug_lse=dbg_l)
+        res["scores"] = dbg_s.cpu().numpy()
+        res["lse"] = dbg_l.cpu().numpy()
+    torch.cuda.synchronize()
+    return res
+
+
+def _check_step(inp, res, scale=None, what=""):
+    ref = oracle.decode_step(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["o_weight"], scale=scale)
+    assert_bf16_close(res["flat"], ref["attn_ref"], what + " attention output")
+    assert_bf16_close(res["out"], ref["out_ref"], what + " projected output")
+    # the projection in isolation: oracle o_proj of the GPU's own attention output. The GPU sums K
+    # products in fp32 and rounds once to bf16, so |gpu - ref| <= K * 2^-24 * sum_k |x_k w_kn| (any
+    # summation order) + one bf16 step of the result.
+    _, iso_ref = oracle.oproj(res["flat"], inp["o_weight"])
+    assert_within_fp32_sum_bound(res["out"], iso_ref, res["flat"], inp["o_weight"], what + " o_proj alone")
+    return ref
+
+
+def test_device_is_gfx950(gpu):
+    props = torch.cuda.get_device_properties(0)
+    assert props.gcnArchName.startswith("gfx950")
+    assert props.multi_processor_count == 256
+    assert props.warp_size == 64
+
+
+@pytest.mark.parametrize("wl", [workloads.TINY, workloads.PAGES], ids=lambda w: w.name)
+def test_decode_workload_small(gpu, wl):
+    inp = workloads.decode_inputs(wl, poison=True)
+    res = _run_step(inp, debug=True)
+    ref = _check_step(inp, res, what=wl.name)
+    att = oracle.attention(inp["q"], inp["k"], inp["v"], inp["seq_lens"], want_scores=True)
+    for b, L in enumerate(inp["seq_lens"]):
+        assert_scores_close(res["scores"][b, :, :L], att["scores"][b, :, :L], wl.name + " scores")
+    np.testing.assert_allclose(res["lse"], att["lse"], rtol=1e-5, atol=1e-5)
+    assert ref is not None
+
+
+@pytest.mark.parametrize("wl", [workloads.BATCHED, workloads.LONG], ids=lambda w: w.name)
+def test_decode_workload_large(gpu, wl):
+    inp = workloads.decode_inputs(wl, poison=True)
+    res = _run_step(inp)
+    _check_step(inp, res, what=wl.name)
+
+
+def test_gemm_f16_workload_bit_exact(gpu):
+    g = workloads.gemm_inputs()
+    c = da.gemm_f16(dev_f16(g["a"]), dev_f16(g["b"]))
+    ref, _ = oracle.gemm_f16(g["a"], g["b"])
+    np.testing.assert_array_equal(host_words(c), ref)
+
+
+def test_gemm_f16_all_ones_golden(gpu):
+    g = workloads.gemm_inputs(all_ones=True)
+    c = host_words(da.gemm_f16(dev_f16(g["a"]), dev_f16(g["b"])))
+    assert np.all(c == 0x6400)  # every entry is exactly k = 1024
+
+
+# ---- edge cases of the attention path ------------------------------------
+
+EDGE = [
+    # (batch, Hq, Hkv, seq_lens, max_seq_len)
+    (1, 4, 1, [1], 1),
+    (1, 4, 1, [2], 2),
+    (1, 1, 1, [33], 40),
+    (2, 2, 1, [16, 17], 17),
+    (3, 8, 2, [1, 129, 700], 700),
+    (2, 6, 2, [127, 128], 300),
+    (2, 32, 2, [300, 5], 300),
+    (1, 16, 2, [4096], 4096),
+    (4, 24, 8, [255, 256, 257, 1000], 1024),
+    (2, 8, 8, [513, 2], 600),
+    (3, 16, 2, [5, 37, 100], 128),   # group 8: last 32-key blocks hold <= 16 keys
+    (2, 16, 1, [17, 48], 48),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "B%d_H%d_KV%d_L%s_Lmax%d" % (c[0], c[1], c[2],
+                                                                                  "-".join(map(str, c[3])), c[4]))
+def test_edge_shapes(gpu, case):
+    B, Hq, Hkv, sl, Lmax = case
+    inp = workloads.custom_decode_inputs(B, Hq, Hkv, sl, max_seq_len=Lmax, hidden=256, seed=sum(sl) + Hq)
+    res = _run_step(inp, debug=True)
+    _check_step(inp, res, what=str(case))
+    att = oracle.attention(inp["q"], inp["k"], inp["v"], inp["seq_lens"], want_scores=True)
+    for b, L in enumerate(sl):
+        assert_scores_close(res["scores"][b, :, :L], att["scores"][b, :, :L], "scores")
+        assert np.all(np.isnan(res["scores"][b, :, L:]))  # nothing written past the sequence
+    np.testing.assert_allclose(res["lse"], att["lse"], rtol=1e-5, atol=1e-5)
+
+
+def test_single_key_is_bit_exact(gpu):
+    inp = workloads.custom_decode_inputs(2, 8, 2, [1, 1], max_seq_len=9, seed=21)
+    res = _run_step(inp)
+    for b in range(2):
+        for qh in range(8):
+            np.testing.assert_array_equal(res["flat"][b, qh * 128:(qh + 1) * 128], inp["v"][b, qh // 4, 0])
+
+
+def test_constant_values_are_bit_exact(gpu):
+    inp = workloads.custom_decode_inputs(1, 8, 2, [3000], seed=22)
+    for h in range(2):
+        inp["v"][0, h, :] = inp["v"][0, h, 7]
+    res = _run_step(inp)
+    for qh in range(8):
+        np.testing.assert_array_equal(res["flat"][0, qh * 128:(qh + 1) * 128], inp["v"][0, qh // 4, 7])
+
+
+def test_softmax_scale_override(gpu):
+    inp = workloads.custom_decode_inputs(2, 8, 2, [200, 77], seed=23)
+    res = _run_step(inp, scale=0.05)
+    _check_step(inp, res, scale=0.05, what="scale 0.05")
+
+
+def test_near_one_hot_in_the_last_split(gpu):
+    # large scores (q x 8) and the dominant key at the very end of a long sequence
+    inp = workloads.custom_decode_inputs(1, 4, 1, [2000], seed=24)
+    qf = bf16_words_to_f64(inp["q"]) * 8
+    inp["q"] = workloads.bf16_words_from_float(qf.astype(np.float32))
+    inp["k"][0, 0, 1999] = workloads.bf16_words_from_float((qf[0, 0] / 8).astype(np.float32))
+    res = _run_step(inp)
+    _check_step(inp, res, what="near one-hot")
+
+
+def test_result_does_not_depend_on_the_split(gpu):
+    # the same sequences under a larger max_seq_len get a different split length
+    base = workloads.custom_decode_inputs(2, 8, 2, [1500, 900], max_seq_len=1500, seed=25)
+    big = dict(base)
+    Lbig = 70000  # 4 (batch, kv head) pairs x 547 splits of 128 exceed the workgroup target
+    for key in ("k", "v"):
+        a = np.full((2, 2, Lbig, 128), workloads.BF16_NAN, np.uint16)
+        a[:, :, :1500] = base[key]
+        big[key] = a
+    p1 = da.decode_attn_plan(da.make_shape(2, 8, 2, 1500, 256))
+    p2 = da.decode_attn_plan(da.make_shape(2, 8, 2, Lbig, 256))
+    r1, r2 = _run_step(base), _run_step(big)
+    ref = _check_step(base, r1, what="Lmax 1500")
+    _check_step(big, r2, what="Lmax 70000")
+    assert (p1.split_len, p1.num_splits) != (p2.split_len, p2.num_splits)
+    assert ref is not None
+
+
+def test_repeat_calls_are_deterministic_and_reuse_the_workspace(gpu):
+    ws = da.Workspace()
+    a = workloads.custom_decode_inputs(3, 16, 4, [700, 1, 333], seed=26)
+    b = workloads.custom_decode_inputs(1, 4, 1, [4000], hidden=512, seed=27)
+    r1 = _run_step(a, ws)
+    r2 = _run_step(b, ws)   # different shape, same (now dirty) workspace
+    r3 = _run_step(a, ws)
+    np.testing.assert_array_equal(r1["out"], r3["out"])
+    np.testing.assert_array_equal(r1["flat"], r3["flat"])
+    _check_step(b, r2, what="after another shape")
+
+
+# ---- the projection alone ------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 3, 8, 15, 16, 20, 33])
+def test_oproj_integer_inputs_bit_exact(gpu, M):
+    rng = np.random.default_rng(100 + M)
+    K, N = 4096, 1024
+    x = workloads.bf16_words_from_float(rng.integers(-1, 1, endpoint=True, size=(M, K)).astype(np.float32))
+    w = workloads.bf16_words_from_float(rng.integers(-1, 1, endpoint=True, size=(K, N)).astype(np.float32))
+    out = host_words(da.oproj_fwd(dev_bf16(x), dev_bf16(w)))
+    ref, _ = oracle.oproj(x, w)
+    np.testing.assert_array_equal(out, ref)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 17])
+def test_oproj_identity_returns_input(gpu, M):
+    rng = np.random.default_rng(200 + M)
+    K = 512
+    x = workloads.bf16_words_from_float(rng.standard_normal((M, K)).astype(np.float32))
+    eye = workloads.bf16_words_from_float(np.eye(K, dtype=np.float32))
+    out = host_words(da.oproj_fwd(dev_bf16(x), dev_bf16(eye)))
+    np.testing.assert_array_equal(out, x)
+
+
+@pytest.mark.parametrize("shape", [(1, 4096, 4096), (4, 8192, 8192), (16, 4096, 4096), (2, 384, 520), (24, 640, 72)])
+def test_oproj_random(gpu, shape):
+    M, K, N = shape
+    rng = np.random.default_rng(M * 7 + N)
+    x = workloads.bf16_words_from_float(rng.standard_normal((M, K)).astype(np.float32) * 0.05)
+    w = workloads.bf16_words_from_float(rng.standard_normal((K, N)).astype(np.float32) * 0.02)
+    out = host_words(da.oproj_fwd(dev_bf16(x), dev_bf16(w)))
+    _, ref = oracle.oproj(x, w)
+    assert_bf16_close(out, ref, "oproj %s" % (shape,))
