@@ -29,8 +29,127 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "µs per decode step (attn+o_proj) and achieved HBM TB/s vs peak, 1×MI355X"
+CALIB_BYTES = 64 * 2 ** 20  # plain device-to-device copy whose HBM traffic is known (read + write)
+PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 1024 * 1024
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: HBM-traffic counters taken from another build are not reused."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "decode_attention_output_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, kernel_prefix: str):
+    """Measured HBM bytes per dispatch of the dominant kernel, from the committed
+    rocprofv3 PMC summary of this workload, if it was taken on the current sources."""
+    path = os.path.join(PROFILES, "pmc_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_hash") != kernel_source_hash() or fields.get("kernel") != kernel_prefix:
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def dominant_kernel(wl, plan, seq_lens):
+    """(kernel name, algorithmic bytes per launch) of the launch that moves the most bytes."""
+    import numpy as np
+
+    s = wl.shape
+    D = s.head_dim
+    attn_bytes = 2 * 2 * s.num_kv_heads * D * int(np.sum(seq_lens)) + 2 * s.batch * s.num_q_heads * D \
+        + 2 * s.batch * s.o_in
+    proj_bytes = 2 * s.o_in * s.hidden + 2 * s.batch * s.o_in + 2 * s.batch * s.hidden
+    if proj_bytes >= attn_bytes:
+        return ("gemv_kernel" if plan.oproj_path == 0 else "gemm_kernel"), proj_bytes, "oproj"
+    return "attn_streamk_kernel", attn_bytes, "attention"
+
+
+def summarize_profile(args):
+    """profiles/pmc_<workload>.txt from a FETCH_SIZE run, a WRITE_SIZE run and a kernel-trace run."""
+    import csv
+
+    import decode_attention_output_amd as da
+    import numpy as np
+    import workloads
+
+    wl = workloads.BY_NAME[args.workload]
+    s = wl.shape
+    seq_lens = workloads.draw_seq_lens(wl, np.random.default_rng(wl.seed))
+    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden))
+    kname, kbytes, _ = dominant_kernel(wl, plan, seq_lens)
+
+    def counter_avg(path, counter, match):
+        vals = []
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter and match(row.get("Kernel_Name", "")):
+                    vals.append(float(row["Counter_Value"]))
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+    is_dom = lambda n: kname in n
+    is_cal = lambda n: "MulFunctor" in n
+    fetch_dom, nf = counter_avg(args.summarize_profile[0], "FETCH_SIZE", is_dom)
+    fetch_cal, _ = counter_avg(args.summarize_profile[0], "FETCH_SIZE", is_cal)
+    write_dom, nw = counter_avg(args.summarize_profile[1], "WRITE_SIZE", is_dom)
+    write_cal, _ = counter_avg(args.summarize_profile[1], "WRITE_SIZE", is_cal)
+    f_scale = (CALIB_BYTES / 1024.0) / fetch_cal if fetch_cal else None
+    w_scale = (CALIB_BYTES / 1024.0) / write_cal if write_cal else None
+    rd = fetch_dom * f_scale * 1024 if fetch_dom is not None and f_scale else None
+    wr = write_dom * w_scale * 1024 if write_dom is not None and w_scale else None
+    stats = []
+    with open(args.summarize_profile[2]) as f:
+        for row in csv.DictReader(f):
+            stats.append((row["Name"], int(row["Calls"]), float(row["AverageNs"]), float(row["MinNs"]),
+                          float(row["MaxNs"])))
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, "pmc_%s.txt" % wl.name)
+    with open(out, "w") as f:
+        f.write("# rocprofv3 summary: %s, workload %s\n" % (kname, wl.name))
+        f.write("# commands (run from the repository root on one MI355X):\n")
+        f.write("#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph\n" % wl.name)
+        f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- "
+                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph --steps 50\n" % wl.name)
+        f.write("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- "
+                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph --steps 50\n" % wl.name)
+        f.write("#   python3 bench.py --workload %s --summarize-profile <fetch csv> <write csv> <stats csv>\n"
+                % wl.name)
+        f.write("# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same counter reads\n")
+        f.write("# for a plain elementwise copy (torch mul by 1.0) of %d MiB read + %d MiB written.\n"
+                % (CALIB_BYTES >> 20, CALIB_BYTES >> 20))
+        f.write("# kernel trace (per kernel: calls, average / min / max ns):\n")
+        for name, calls, avg, mn, mx in stats:
+            f.write("#   %-90s %6d %12.1f %12.1f %12.1f\n" % (name[:90], calls, avg, mn, mx))
+        f.write("kernel = %s\n" % kname)
+        f.write("source_hash = %s\n" % kernel_source_hash())
+        f.write("algorithmic_bytes_per_dispatch = %d\n" % kbytes)
+        f.write("dispatches_counted = %d / %d\n" % (nf, nw))
+        f.write("fetch_kib_per_dispatch = %s\n" % fetch_dom)
+        f.write("write_kib_per_dispatch = %s\n" % write_dom)
+        f.write("fetch_scale = %s\nwrite_scale = %s\n" % (f_scale, w_scale))
+        f.write("hbm_read_bytes_per_dispatch = %s\n" % (None if rd is None else int(rd)))
+        f.write("hbm_write_bytes_per_dispatch = %s\n" % (None if wr is None else int(wr)))
+        f.write("hbm_bytes_per_dispatch = %s\n" % (None if rd is None or wr is None else int(rd + wr)))
+        dom_avg = [avg for name, _, avg, _, _ in stats if kname in name]
+        f.write("trace_avg_ns = %s\n" % (dom_avg[0] if dom_avg else None))
+    print(out)
 
 
 def parse():
@@ -46,11 +165,17 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "TRACE_STATS_CSV"),
+                    help="write the PMC/trace summary of a profiled run to profiles/ and exit")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE %d) is not supported. "
@@ -90,58 +215,84 @@ def main():
         st["ws"] = da.Workspace(dev)
         sets.append(st)
     del inp["k"], inp["v"]  # host copies of the cache are reloaded below only if needed
-    stream = torch.cuda.current_stream()
+    # every launch goes to one dedicated stream (a graph must be captured on a non-default stream)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(stream)
 
-    def step(st):
-        da.decode_attn_fwd(st["q"], st["k"], st["v"], sl, st["o_weight"], out=st["out"], workspace=st["ws"])
+    for st in sets:
+        st["step"] = da.DecodeStep(st["q"], st["k"], st["v"], sl, st["o_weight"], out=st["out"], workspace=st["ws"],
+                                   stream=stream)
 
     plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden))
 
-    # ---- warm-up, then exactly `steps` timed steps ----
+    # ---- warm-up, then exactly `steps` timed steps (one prepared C-ABI call each) ----
     for i in range(args.warmup):
-        step(sets[i % R])
+        sets[i % R]["step"]()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(sets[i % R])
-        ev[i][1].record(stream)
+        sets[i % R]["step"]()
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_us = (t1 - t0) / args.steps * 1e6
-    ev_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
-    step_us = statistics.median(ev_us)
+    gpu_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
 
-    # ---- per-kernel pass: the attention launches and the projection launch ----
+    # ---- the same steps replayed from a HIP graph (no host work per step) ----
+    graph_us = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(args.steps):
+                sets[i % R]["step"]()
+        torch.cuda.synchronize()
+        g.replay()  # first replay uploads the graph
+        torch.cuda.synchronize()
+        gv0, gv1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gv0.record(stream)
+        g.replay()
+        gv1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = gv0.elapsed_time(gv1) * 1e3 / args.steps
+        del g
+
+    # ---- per-kernel pass: the attention launch and the projection launch ----
     n_b = args.breakdown_steps
     ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_b)]
     ev_o = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_b)]
+    for st in sets:
+        st["attn"] = da.AttentionStep(st["q"], st["k"], st["v"], sl, out=st["flat"], workspace=st["ws"], stream=stream)
+        st["proj"] = da.OprojStep(st["flat"], st["o_weight"], out=st["out"], workspace=st["ws"], stream=stream)
     for i in range(n_b):
-        st = sets[i % R]
         ev_a[i][0].record(stream)
-        da.decode_attn_only(st["q"], st["k"], st["v"], sl, out=st["flat"], workspace=st["ws"])
+        sets[i % R]["attn"]()
         ev_a[i][1].record(stream)
     for i in range(n_b):
-        st = sets[i % R]
         ev_o[i][0].record(stream)
-        da.oproj_fwd(st["flat"], st["o_weight"], out=st["out"], workspace=st["ws"])
+        sets[i % R]["proj"]()
         ev_o[i][1].record(stream)
     torch.cuda.synchronize()
-    attn_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in ev_a)
-    oproj_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in ev_o)
+    attn_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev_a)
+    oproj_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev_o)
     # restore the step's own output in set 0 for the parity check
-    step(sets[0])
+    sets[0]["step"]()
     torch.cuda.synchronize()
 
-    attn_bytes = kv_read + 2 * s.batch * s.num_q_heads * D + 2 * s.batch * s.o_in
-    proj_bytes = w_bytes + 2 * s.batch * s.o_in + 2 * s.batch * s.hidden
-    if proj_bytes >= attn_bytes:
-        dom = {"kernel": "gemv_kernel (o_proj, VALU)" if plan.oproj_path == 0 else "gemm_kernel (o_proj, MFMA)",
-               "bytes": proj_bytes, "us": oproj_us}
-    else:
-        dom = {"kernel": "attn_split_kernel + attn_combine_kernel", "bytes": attn_bytes, "us": attn_us}
-    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    kname, kbytes, which = dominant_kernel(wl, plan, seq_lens)
+    dom_us = oproj_us if which == "oproj" else attn_us
+    achieved = kbytes / (dom_us * 1e-6) / 1e9
+    traffic = traffic_from_profile(wl.name, kname)
+
+    # a plain elementwise copy of known size, outside the timed region: the HBM
+    # counters of a profiled run are scaled by what they read for it
+    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    torch.mul(calib_src, 1.0, out=calib_dst)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     result = {
         "metric": METRIC,
@@ -152,7 +303,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(wall_us / 1e3, 6),
         "us_per_step": round(wall_us, 3),
-        "us_per_step_events_median": round(step_us, 3),
+        "us_per_step_gpu_events": round(gpu_us, 3),
+        "us_per_step_graph_replay": None if graph_us is None else round(graph_us, 3),
         "frac_of_hbm_peak": round(alg_bytes / (wall_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -169,14 +321,15 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": dom["kernel"],
+            "kernel": kname,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "avg_launch_us": round(dom["us"], 3),
-            "alg_bytes_per_launch": dom["bytes"],
+            "traffic": traffic,
+            "avg_launch_us": round(dom_us, 3),
+            "alg_bytes_per_launch": kbytes,
+            "timing": "median of %d HIP-event pairs around single launches on the bench stream" % n_b,
         },
         "breakdown_us": {"attention": round(attn_us, 3), "oproj": round(oproj_us, 3)},
     }

@@ -277,3 +277,80 @@ def gemm_f16(a, b, c=None, stream=None):
     if rc != DA_OK:
         raise DecodeAttnError(rc, "gemm_f16")
     return c
+
+
+class PreparedCall:
+    """One C-ABI call with its arguments marshalled in advance, so that each
+    invocation costs a single ctypes call. Keeps every tensor it refers to
+    alive. Invocations that share a workspace must stay ordered on one stream."""
+
+    def __init__(self, fn, args, what, keep, result):
+        self._fn, self._args, self._what, self._keep, self.result = fn, args, what, keep, result
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != DA_OK:
+            raise DecodeAttnError(rc, self._what)
+        return self.result
+
+
+def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what):
+    B, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale)
+    need = decode_attn_workspace_size(shape)
+    if need == 0:
+        raise DecodeAttnError(DA_ERR_SHAPE, what)
+    ws = (workspace or Workspace(q.device)).get(need)
+    shape.workspace = _ptr(ws)
+    shape.workspace_bytes = ws.numel()
+    return shape, ws
+
+
+def DecodeStep(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Optional[Workspace] = None,
+               softmax_scale: float = 0.0, stream=None) -> PreparedCall:
+    """A prepared ``decode_attn_fwd``; calling it runs one decode step and returns ``out``."""
+    torch = _check_dev("q", q, _torch().bfloat16)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("o_weight", o_weight)):
+        _check_dev(name, t, torch.bfloat16)
+    _check_dev("seq_lens", seq_lens, torch.int32)
+    if out is None:
+        out = torch.empty((q.shape[0], o_weight.shape[1]), dtype=torch.bfloat16, device=q.device)
+    shape, ws = _prepare_shape(q, k_cache, o_weight.shape[1], softmax_scale, workspace, "decode_attn_fwd")
+    tensors = (q, k_cache, v_cache, seq_lens, o_weight, out)
+    args = [ctypes.c_void_p(t.data_ptr()) for t in tensors] + [ctypes.byref(shape),
+                                                              ctypes.c_void_p(_stream_handle(stream))]
+    return PreparedCall(load_library().decode_attn_fwd, args, "decode_attn_fwd", (tensors, shape, ws), out)
+
+
+def AttentionStep(q, k_cache, v_cache, seq_lens, out=None, workspace: Optional[Workspace] = None,
+                  softmax_scale: float = 0.0, stream=None) -> PreparedCall:
+    """A prepared ``decode_attn_only``; calling it returns the bf16 [B, Hq*D] attention output."""
+    torch = _check_dev("q", q, _torch().bfloat16)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_dev(name, t, torch.bfloat16)
+    _check_dev("seq_lens", seq_lens, torch.int32)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq * D), dtype=torch.bfloat16, device=q.device)
+    shape, ws = _prepare_shape(q, k_cache, 8, softmax_scale, workspace, "decode_attn_only")
+    tensors = (q, k_cache, v_cache, seq_lens, out)
+    args = [ctypes.c_void_p(t.data_ptr()) for t in tensors] + [ctypes.byref(shape),
+                                                              ctypes.c_void_p(_stream_handle(stream))]
+    return PreparedCall(load_library().decode_attn_only, args, "decode_attn_only", (tensors, shape, ws), out)
+
+
+def OprojStep(x, w, out=None, workspace: Optional[Workspace] = None, stream=None) -> PreparedCall:
+    """A prepared ``oproj_fwd``; calling it returns out = x @ w (bf16)."""
+    torch = _check_dev("x", x, _torch().bfloat16)
+    _check_dev("w", w, torch.bfloat16)
+    M, K = x.shape
+    N = w.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    need = oproj_workspace_size(M, K, N)
+    ws = (workspace or Workspace(x.device)).get(need)
+    args = [ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_int32(M), ctypes.c_int32(K), ctypes.c_int32(N), ctypes.c_void_p(_ptr(ws)),
+            ctypes.c_size_t(0 if ws is None else ws.numel()), ctypes.c_void_p(_stream_handle(stream))]
+    return PreparedCall(load_library().oproj_fwd, args, "oproj_fwd", ((x, w, out), ws), out)

@@ -23,7 +23,8 @@ using da::kHeadDim;
 
 constexpr int kAttnWorkgroups = 512;        // stream-K attention: two per compute unit
 constexpr int kAttnBlockKeys = 32;          // keys per wave step
-constexpr int kTargetProjWorkgroups = 256;   // one per compute unit
+constexpr int kTargetProjWorkgroups = 512;   // GEMV: two per compute unit
+constexpr int kTargetGemmWorkgroups = 512;   // MFMA GEMM: two per compute unit
 constexpr int kGemvUnroll = 8;               // weight rows per lane in flight
 constexpr int kGemmKStep = 128;
 constexpr size_t kAlign = 256;
@@ -64,20 +65,22 @@ struct ProjPlan {
 ProjPlan plan_proj(int M, int K, int N) {
   ProjPlan pp{};
   if (M < 16) {
-    // GEMV: the widest column tile the accumulators allow (a wave then reads
-    // whole KiB-long row pieces), never much wider than N itself; the K axis
-    // is cut so that about kTargetProjWorkgroups workgroups stream the weight.
+    // GEMV: 64-column strips (a 128-byte line of each weight row per
+    // workgroup) and a K-chunk sized so that about kTargetProjWorkgroups
+    // workgroups stream the weight; every lane keeps 8 rows in flight.
     pp.path = 0;
     pp.mpad = pow2_at_least(M);
-    int tc = pp.mpad <= 4 ? 512 : (pp.mpad <= 8 ? 256 : 128);
-    while (tc > 64 && tc / 2 >= N) tc /= 2;
+    // widest tile (up to 256 columns) that still leaves 32 column tiles
+    int tc = 256;
+    while (tc > 64 && (N / tc < 32 || pp.mpad * tc > 2048)) tc /= 2;
     pp.tile_n = tc;
     pp.tiles = ceil_div(N, tc);
-    const int gran = (2048 / tc) * kGemvUnroll;  // rows one pass of the workgroup covers
+    const int gran = (2048 / tc) * kGemvUnroll;  // rows of one batch of the workgroup
     int ksplit = std::max(1, kTargetProjWorkgroups / pp.tiles);
     ksplit = std::min(ksplit, std::max(1, ceil_div(K, gran)));
     int kchunk = (int)align_up((size_t)ceil_div(K, ksplit), gran);
-    const int max_chunk = 32768 / (4 * pp.mpad);  // activations of a chunk fit 32 KiB of LDS
+    // activations of a chunk + the reduction buffers fit 64 KiB of LDS
+    const int max_chunk = (65536 - 4096 - 16 * pp.mpad * tc) / (4 * pp.mpad);
     kchunk = std::min(kchunk, std::max(gran, max_chunk / gran * gran));
     pp.kchunk = kchunk;
     pp.ksplit = ceil_div(K, kchunk);
@@ -86,7 +89,7 @@ ProjPlan plan_proj(int M, int K, int N) {
     pp.mpad = 16;
     pp.tile_n = 64;
     pp.tiles = ceil_div(N, 64) * ceil_div(M, 16);
-    int ksplit = std::max(1, kTargetProjWorkgroups / pp.tiles);
+    int ksplit = std::max(1, kTargetGemmWorkgroups / pp.tiles);
     ksplit = std::min(ksplit, std::max(1, K / kGemmKStep));
     pp.kchunk = (int)align_up((size_t)ceil_div(K, ksplit), kGemmKStep);
     pp.ksplit = ceil_div(K, pp.kchunk);
@@ -110,7 +113,9 @@ AttnPlan plan_attn(const decode_attn_shape_t* s) {
   ap.gpad = pow2_at_least(G);
   const long pairs = (long)s->batch * s->num_kv_heads;
   const long blocks_max = pairs * ceil_div(s->max_seq_len, kAttnBlockKeys);
-  ap.workgroups = (int)std::min<long>(kAttnWorkgroups, blocks_max);
+  // about four blocks (128 keys) per workgroup at least: short problems are
+  // latency bound and gain nothing from more, smaller pieces
+  ap.workgroups = (int)std::max<long>(1, std::min<long>(kAttnWorkgroups, blocks_max / 4));
   ap.keys_per_wg = ceil_div(blocks_max, ap.workgroups) * kAttnBlockKeys;
   ap.slots = (size_t)ap.workgroups + (size_t)pairs;
   ap.part_o_bytes = align_up(ap.slots * G * kHeadDim * sizeof(float), kAlign);
@@ -220,6 +225,7 @@ int run_proj(const ProjPlan& pp, const void* x, const void* w, void* out, int M,
     g.kchunk = pp.kchunk;
     g.ksplit = pp.ksplit;
     g.tile_n = pp.tile_n;
+    g.part_bytes = (uint32_t)std::min<size_t>(pp.part_bytes, 0xffffffffu);
     return da::launch_gemv(g, pp.mpad, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
   }
   da::GemmParams g{};
@@ -233,6 +239,7 @@ int run_proj(const ProjPlan& pp, const void* x, const void* w, void* out, int M,
   g.N = N;
   g.kchunk = pp.kchunk;
   g.ksplit = pp.ksplit;
+  g.part_bytes = (uint32_t)std::min<size_t>(pp.part_bytes, 0xffffffffu);
   return da::launch_gemm_bf16(g, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 

@@ -40,10 +40,11 @@ struct GemvParams {
   const uint16_t* w;  // bf16 [K, N]
   uint16_t* out;      // bf16 [M, N]
   float* part;        // fp32 [ksplit, M, N] (ksplit > 1)
-  uint32_t* counters; // [ceil(N / tile_n)] arrival counters (ksplit > 1)
+  uint32_t part_bytes;
+  uint32_t* counters; // [ceil(N / 64)] arrival counters (ksplit > 1)
   int M, K, N;
   int kchunk, ksplit;
-  int tile_n;         // output columns per workgroup: 64, 128, 256 or 512
+  int tile_n;         // output columns per workgroup (64)
 };
 
 // C[M, N] = A[M, K] @ B[K, N] on MFMA, 16 x 64 output tile per workgroup.
@@ -52,6 +53,7 @@ struct GemmParams {
   const uint16_t* b;  // [K, N]
   uint16_t* c;        // [M, N]
   float* part;        // fp32 [ksplit, M, N] (ksplit > 1)
+  uint32_t part_bytes;
   uint32_t* counters; // [ceil(M/16) * N/64] arrival counters (ksplit > 1)
   int M, K, N;
   int kchunk, ksplit;

@@ -16,7 +16,7 @@
 // tile is transposed through LDS into the operand layout (B needs 8
 // consecutive k per lane, the weight is row-major in n), the activation
 // fragment is read straight from global memory.
-#include "gfx950.hpp"
+#include "attn_core.hpp"
 #include "kernels.hpp"
 
 namespace da {
@@ -24,53 +24,50 @@ namespace da {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;  // weight rows per lane in flight per pass
+constexpr int kUnroll = 8;                 // weight rows per lane per batch (128 B in flight per lane)
 
-// Workgroup tile of the GEMV: TC output columns (TC/8 lanes of 16 bytes per
-// weight row, so a wave reads 1 KiB of contiguous rows when TC = 512) times a
-// K-chunk of rows; MB activation rows are held per lane.
+// GEMV workgroup: a TC-column tile of the weight (TC*2 bytes of every row)
+// times a K-chunk of rows. Lane t streams 16-byte pieces of rows rr, rr+RPP,
+// ... (rr = t/(TC/8)) of column group t%(TC/8), a batch of kUnroll rows at a
+// time with the next batch in flight while the current one is multiplied.
+// The activation chunk is staged in LDS (as fp32) after the first weight
+// batch has been issued.
 template <int MB, int TC>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
-  constexpr int LPR = TC / 8;             // lanes per weight row
-  constexpr int RPP = kThreads / LPR;     // rows per pass of the workgroup
-  constexpr int RPW = kWave / LPR > 0 ? kWave / LPR : 1;  // row lanes inside one wave
-  extern __shared__ float s_x[];          // [kchunk][MB] activations of this K-chunk, fp32
-  __shared__ float s_red[kThreads / kWave][MB][TC];
+  constexpr int kStrip = TC;
+  constexpr int kLanesPerRow = TC / 8;
+  constexpr int kRowLanes = kThreads / kLanesPerRow;
+  extern __shared__ float s_x[];  // [kchunk][MB]
+  __shared__ float s_red[kThreads / kWave][MB][kStrip];
+  __shared__ float4 s_fin[kThreads];
 
   const int tile = blockIdx.x, ks = blockIdx.y;
-  const int n0 = tile * TC;
+  const int n0 = tile * kStrip;
   const int k0 = ks * p.kchunk;
   const int kn = min(p.kchunk, p.K - k0);
   const int t = threadIdx.x;
-  const int cg = t % LPR;  // 8-column group inside the tile
-  const int rr = t / LPR;  // row lane
+  const int cg = t % kLanesPerRow, rr = t / kLanesPerRow;
   const int n = n0 + cg * 8;
   const bool col_ok = n < p.N;
+  const uint16_t* __restrict__ wbase = p.w + (size_t)k0 * p.N + n;
+  const int nbatch = (kn + kRowLanes * kUnroll - 1) / (kRowLanes * kUnroll);
 
-  for (int idx = t; idx < MB * kn; idx += kThreads) {
-    const int m = idx / kn, kk = idx % kn;
-    const uint16_t xw = (m < p.M) ? p.x[(size_t)m * p.K + k0 + kk] : (uint16_t)0;
-    s_x[kk * MB + m] = __builtin_bit_cast(float, (uint32_t)xw << 16);
-  }
-  __syncthreads();
-
+  auto load_batch = [&](uint4 (&wv)[kUnroll], int bt) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int kk = bt * kRowLanes * kUnroll + rr + kRowLanes * u;
+      wv[u] = (col_ok && kk < kn) ? ld16(wbase + (size_t)kk * p.N) : make_uint4(0, 0, 0, 0);
+    }
+  };
   float acc[MB][8];
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
-
-  const uint16_t* __restrict__ wbase = p.w + (size_t)k0 * p.N + n;
-  for (int base = 0; base < kn; base += RPP * kUnroll) {
-    uint4 wv[kUnroll];
+  auto use_batch = [&](const uint4 (&wv)[kUnroll], int bt) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int kk = base + rr + RPP * u;
-      wv[u] = (col_ok && kk < kn) ? ld16(wbase + (size_t)kk * p.N) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int kk = base + rr + RPP * u;
+      const int kk = bt * kRowLanes * kUnroll + rr + kRowLanes * u;
       if (kk < kn) {
         float wf[8];
         unpack_bf16x8(wv[u], wf);
@@ -82,54 +79,127 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
         }
       }
     }
+  };
+
+  uint4 wa[kUnroll], wb[kUnroll];
+  load_batch(wa, 0);
+  for (int idx = t; idx < MB * kn; idx += kThreads) {
+    const int m = idx / kn, kk = idx % kn;
+    const uint16_t xw = (m < p.M) ? p.x[(size_t)m * p.K + k0 + kk] : (uint16_t)0;
+    s_x[kk * MB + m] = __builtin_bit_cast(float, (uint32_t)xw << 16);
+  }
+  __syncthreads();
+  for (int bt = 0; bt < nbatch; bt += 2) {
+    if (bt + 1 < nbatch) load_batch(wb, bt + 1);
+    use_batch(wa, bt);
+    if (bt + 1 >= nbatch) break;
+    if (bt + 2 < nbatch) load_batch(wa, bt + 2);
+    use_batch(wb, bt + 1);
   }
 
-  // reduce the row lanes of a wave (lanes l, l^LPR, l^2LPR, ...), then the waves
+  // reduce the row lanes of a wave (lanes l, l^LPR, l^2LPR, ...), then the 4 waves
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float v = acc[m][e];
 #pragma unroll
-      for (int x = LPR; x < kWave; x <<= 1) v += __shfl_xor(v, x);
+      for (int x = kLanesPerRow; x < kWave; x <<= 1) v += __shfl_xor(v, x);
       acc[m][e] = v;
     }
   const int wave = t / kWave, lane = t % kWave;
-  if (lane < LPR) {
+  if (lane < kLanesPerRow) {
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_red[wave][m][lane * 8 + e] = acc[m][e];
+    for (int m = 0; m < MB; ++m) {
+      *reinterpret_cast<float4*>(&s_red[wave][m][lane * 8]) = make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
+      *reinterpret_cast<float4*>(&s_red[wave][m][lane * 8 + 4]) =
+          make_float4(acc[m][4], acc[m][5], acc[m][6], acc[m][7]);
+    }
   }
-  (void)RPW;
   __syncthreads();
 
+  // 16 groups of 4 columns per activation row
   const int M = p.M;
-  float* part = p.part;
-  for (int idx = t; idx < M * TC; idx += kThreads) {
-    const int m = idx / TC, c = idx % TC;
-    if (n0 + c >= p.N) continue;
-    const float v = s_red[0][m][c] + s_red[1][m][c] + s_red[2][m][c] + s_red[3][m][c];
-    if (p.ksplit == 1)
-      p.out[(size_t)m * p.N + n0 + c] = f32_to_bf16_rne(v);
-    else
-      store_coherent(&part[((size_t)ks * M + m) * p.N + n0 + c], v);
+  const int npairs = M * (kStrip / 4);
+  const rsrc_t part = make_rsrc(p.part, p.part_bytes);
+  for (int pr = t; pr < npairs; pr += kThreads) {
+    const int m = pr / (kStrip / 4), c4 = pr % (kStrip / 4);
+    float4 v = *reinterpret_cast<const float4*>(&s_red[0][m][c4 * 4]);
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) {
+      const float4 o = *reinterpret_cast<const float4*>(&s_red[w][m][c4 * 4]);
+      v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+    }
+    const int col = n0 + c4 * 4;
+    if (col >= p.N) continue;
+    if (p.ksplit == 1) {
+      const uint32_t w01 = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+      const uint32_t w23 = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+      *reinterpret_cast<uint2*>(p.out + (size_t)m * p.N + col) = make_uint2(w01, w23);
+    } else {
+      rsrc_st16_coherent(part, (uint32_t)((((size_t)ks * M + m) * p.N + col) * 4),
+                         make_uint4(__builtin_bit_cast(uint32_t, v.x), __builtin_bit_cast(uint32_t, v.y),
+                                    __builtin_bit_cast(uint32_t, v.z), __builtin_bit_cast(uint32_t, v.w)));
+    }
   }
   if (p.ksplit == 1) return;
   if (!arrive_last_coherent(&p.counters[tile], (uint32_t)p.ksplit)) return;
-  for (int idx = t; idx < M * TC; idx += kThreads) {
-    const int m = idx / TC, c = idx % TC;
-    if (n0 + c >= p.N) continue;
-    float v = 0.f;
-    for (int s = 0; s < p.ksplit; ++s) v += load_coherent(&part[((size_t)s * M + m) * p.N + n0 + c]);
-    p.out[(size_t)m * p.N + n0 + c] = f32_to_bf16_rne(v);
+
+  // last K-chunk of the strip: add the partials of all chunks, in chunk order per phase
+  for (int base = 0; base < npairs; base += kThreads) {
+    const int cnt = min(npairs - base, kThreads);
+    const int nph = kThreads / cnt;
+    const int pr = base + t % cnt, ph = t / cnt;
+    const int m = pr / (kStrip / 4), c4 = pr % (kStrip / 4);
+    const int col = n0 + c4 * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ph < nph && col < p.N) {
+      for (int s0 = ph; s0 < p.ksplit; s0 += 8 * nph) {
+        uint4 pv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int sidx = min(s0 + u * nph, p.ksplit - 1);
+          pv[u] = rsrc_ld16_coherent(part, (uint32_t)((((size_t)sidx * M + m) * p.N + col) * 4));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (s0 + u * nph < p.ksplit) {
+            v.x += __builtin_bit_cast(float, pv[u].x);
+            v.y += __builtin_bit_cast(float, pv[u].y);
+            v.z += __builtin_bit_cast(float, pv[u].z);
+            v.w += __builtin_bit_cast(float, pv[u].w);
+          }
+        }
+      }
+    }
+    s_fin[t] = v;
+    __syncthreads();
+    if (t < cnt && col < p.N) {
+      float4 f = s_fin[t];
+      for (int q2 = 1; q2 < nph; ++q2) {
+        const float4 o = s_fin[t + q2 * cnt];
+        f.x += o.x; f.y += o.y; f.z += o.z; f.w += o.w;
+      }
+      const uint32_t w01 = (uint32_t)f32_to_bf16_rne(f.x) | ((uint32_t)f32_to_bf16_rne(f.y) << 16);
+      const uint32_t w23 = (uint32_t)f32_to_bf16_rne(f.z) | ((uint32_t)f32_to_bf16_rne(f.w) << 16);
+      *reinterpret_cast<uint2*>(p.out + (size_t)m * p.N + col) = make_uint2(w01, w23);
+    }
+    __syncthreads();
   }
 }
 
 // ---- MFMA GEMM: 16 x 64 output tile, K staged 128 rows at a time ----
+//
+// The MFMA operands need 8 consecutive k per lane, while the weight is
+// row-major in n: each 128-row step of the weight tile is stored in LDS as
+// loaded ([k][n], 16-byte writes) and read back transposed, eight 16-bit reads
+// per lane per operand. The activation step is staged in LDS as [m][k] and
+// read with one 16-byte read per operand. The global loads of step s+1 are in
+// flight while step s is multiplied.
 constexpr int kStrip = 64;
 constexpr int kKStep = 128;
-constexpr int kBtPitch = kKStep + 8;  // bf16 elements per transposed row (pad vs bank conflicts)
+constexpr int kBPitch = kStrip + 8;  // bf16 per weight row in LDS
+constexpr int kAPitch = kKStep + 8;  // bf16 per activation row in LDS
 
 template <bool F16>
 __device__ __forceinline__ uint16_t to_out(float v) {
@@ -142,45 +212,55 @@ __device__ __forceinline__ uint16_t to_out(float v) {
 
 template <bool F16>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
-  __shared__ uint16_t s_bt[kStrip][kBtPitch];  // B tile transposed: [n][k]
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[kKStep][kBPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[16][kAPitch];
+  __shared__ float4 s_fin[kThreads];
 
   const int nt = blockIdx.x, mt = blockIdx.y, ks = blockIdx.z;
   const int n0 = nt * kStrip, m0 = mt * 16;
   const int k0 = ks * p.kchunk;
   const int kn = min(p.kchunk, p.K - k0);
+  const int nsteps = (kn + kKStep - 1) / kKStep;
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int col = lane & 15, grp = lane >> 4;
-  const int arow = m0 + col;
-  const bool arow_ok = arow < p.M;
-  const int bcg = t & 7;   // 8-column group this lane loads
-  const int brow = t >> 3; // first of the 4 rows this lane loads
+  const int bcg = t & 7;    // 8-column group this lane loads
+  const int brow = t >> 3;  // first of the 4 weight rows this lane loads
   const bool bcol_ok = n0 + bcg * 8 < p.N;
+  const int am = t >> 4, ak = (t & 15) * 8;  // activation element this lane loads
+  const bool arow_ok = m0 + am < p.M;
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < kn; kb += kKStep) {
+  uint4 bv[4], av;
+  auto load_step = [&](int st) {
+    const int kb = st * kKStep;
     const int rows = min(kKStep, kn - kb);
-    uint4 bv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = brow + 32 * j;
       bv[j] = (bcol_ok && r < rows) ? ld16(p.b + (size_t)(k0 + kb + r) * p.N + n0 + bcg * 8) : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();  // previous tile fully consumed
+    av = (arow_ok && ak < rows) ? ld16(p.a + (size_t)(m0 + am) * p.K + k0 + kb + ak) : make_uint4(0, 0, 0, 0);
+  };
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  load_step(0);
+  for (int st = 0; st < nsteps; ++st) {
+    __syncthreads();  // the previous step is no longer read
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = brow + 32 * j;
-      const uint32_t w4[4] = {bv[j].x, bv[j].y, bv[j].z, bv[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s_bt[bcg * 8 + 2 * e][r] = (uint16_t)(w4[e] & 0xffffu);
-        s_bt[bcg * 8 + 2 * e + 1][r] = (uint16_t)(w4[e] >> 16);
-      }
-    }
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&s_b[brow + 32 * j][bcg * 8]) = bv[j];
+    *reinterpret_cast<uint4*>(&s_a[am][ak]) = av;
     __syncthreads();
+    if (st + 1 < nsteps) load_step(st + 1);
+    const int rows = min(kKStep, kn - st * kKStep);
     for (int sub = 0; sub < rows; sub += 32) {
-      const int k = k0 + kb + sub + grp * 8;
-      const uint4 a = arow_ok ? ld16(p.a + (size_t)arow * p.K + k) : make_uint4(0, 0, 0, 0);
-      const uint4 bb = *reinterpret_cast<const uint4*>(&s_bt[wave * 16 + col][sub + grp * 8]);
+      const uint4 a = *reinterpret_cast<const uint4*>(&s_a[col][sub + grp * 8]);
+      uint32_t bw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = s_b[sub + grp * 8 + 2 * j][wave * 16 + col];
+        const uint32_t hi = s_b[sub + grp * 8 + 2 * j + 1][wave * 16 + col];
+        bw[j] = lo | (hi << 16);
+      }
+      const uint4 bb = make_uint4(bw[0], bw[1], bw[2], bw[3]);
       if constexpr (F16)
         acc = mfma_f16(a, bb, acc);
       else
@@ -199,22 +279,38 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     }
     return;
   }
+  const rsrc_t part = make_rsrc(p.part, p.part_bytes);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = m0 + grp * 4 + r;
-    if (m < p.M && cn_ok) store_coherent(&p.part[((size_t)ks * p.M + m) * p.N + cn], acc[r]);
+    if (m < p.M && cn_ok) rsrc_st4f_coherent(part, (uint32_t)((((size_t)ks * p.M + m) * p.N + cn) * 4), acc[r]);
   }
   const int tile = mt * gridDim.x + nt;
   if (!arrive_last_coherent(&p.counters[tile], (uint32_t)p.ksplit)) return;
+  // the last K-chunk adds every chunk's partial; lane (r, n) of the tile, splits in 8-wide batches
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < p.ksplit; s0 += 8) {
+    float pv[8][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = min(m0 + grp * 4 + r, p.M - 1);
+        const int sidx = min(s0 + u, p.ksplit - 1);
+        pv[u][r] = rsrc_ld4f_coherent(part, (uint32_t)((((size_t)sidx * p.M + m) * p.N + min(cn, p.N - 1)) * 4));
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < p.ksplit)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += pv[u][r];
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = m0 + grp * 4 + r;
-    if (m < p.M && cn_ok) {
-      float v = 0.f;
-      for (int s = 0; s < p.ksplit; ++s) v += load_coherent(&p.part[((size_t)s * p.M + m) * p.N + cn]);
-      p.c[(size_t)m * p.N + cn] = to_out<F16>(v);
-    }
+    if (m < p.M && cn_ok) p.c[(size_t)m * p.N + cn] = to_out<F16>(v[r]);
   }
+  (void)s_fin;
 }
 
 }  // namespace

@@ -142,9 +142,10 @@ def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
     keys = cfg["batch"] * cfg["num_kv_heads"] * cfg["max_seq_len"]
     assert plan.split_len % 32 == 0 and plan.split_len * plan.num_splits >= keys
     assert plan.split_len * (plan.num_splits - 1) < keys + 32 * plan.num_splits
-    # every matmul gets enough workgroups to occupy the 256 compute units when the problem allows it
-    if keys >= 256 * 32:
-        assert plan.qk.workgroups >= 256
+    # the keys are spread over enough workgroups for the 256 compute units when the problem allows
+    # it, but never so many that a workgroup streams fewer than 128 keys
+    assert plan.qk.workgroups >= min(256, keys // 128)
+    assert plan.split_len >= min(128, 32 * (-(-keys // 32)))
     assert plan.oproj.workgroups >= min(256, (cfg["hidden"] // 64) * (cfg["num_q_heads"] * 128 // 256))
     # projection path: VALU GEMV below 16 rows, MFMA from 16 rows
     assert plan.oproj_path == (1 if cfg["batch"] >= 16 else 0)
