@@ -67,6 +67,12 @@ def traffic_from_profile(workload: str, kernel_prefix: str):
         return None
 
 
+def workloads_alg_bytes(shape, seq_lens):
+    import workloads
+
+    return workloads.algorithmic_bytes(shape, seq_lens)
+
+
 def dominant_kernel(wl, plan, seq_lens):
     """(kernel name, algorithmic bytes per launch) of the launch that moves the most bytes."""
     import numpy as np
@@ -76,6 +82,9 @@ def dominant_kernel(wl, plan, seq_lens):
     attn_bytes = 2 * 2 * s.num_kv_heads * D * int(np.sum(seq_lens)) + 2 * s.batch * s.num_q_heads * D \
         + 2 * s.batch * s.o_in
     proj_bytes = 2 * s.o_in * s.hidden + 2 * s.batch * s.o_in + 2 * s.batch * s.hidden
+    if plan.fused:
+        # one launch carries the whole step
+        return "decode_step_kernel", workloads_alg_bytes(s, seq_lens), "step"
     if proj_bytes >= attn_bytes:
         return ("gemv_kernel" if plan.oproj_path == 0 else "gemm_kernel"), proj_bytes, "oproj"
     return "attn_streamk_kernel", attn_bytes, "attention"
@@ -263,6 +272,11 @@ def main():
     n_b = args.breakdown_steps
     ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_b)]
     ev_o = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_b)]
+    ev_s = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_b)]
+    for i in range(n_b):
+        ev_s[i][0].record(stream)
+        sets[i % R]["step"]()
+        ev_s[i][1].record(stream)
     for st in sets:
         st["attn"] = da.AttentionStep(st["q"], st["k"], st["v"], sl, out=st["flat"], workspace=st["ws"], stream=stream)
         st["proj"] = da.OprojStep(st["flat"], st["o_weight"], out=st["out"], workspace=st["ws"], stream=stream)
@@ -277,12 +291,13 @@ def main():
     torch.cuda.synchronize()
     attn_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev_a)
     oproj_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev_o)
+    step_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev_s)
     # restore the step's own output in set 0 for the parity check
     sets[0]["step"]()
     torch.cuda.synchronize()
 
     kname, kbytes, which = dominant_kernel(wl, plan, seq_lens)
-    dom_us = oproj_us if which == "oproj" else attn_us
+    dom_us = {"oproj": oproj_us, "attention": attn_us, "step": step_us}[which]
     achieved = kbytes / (dom_us * 1e-6) / 1e9
     traffic = traffic_from_profile(wl.name, kname)
 
@@ -331,7 +346,8 @@ def main():
             "alg_bytes_per_launch": kbytes,
             "timing": "median of %d HIP-event pairs around single launches on the bench stream" % n_b,
         },
-        "breakdown_us": {"attention": round(attn_us, 3), "oproj": round(oproj_us, 3)},
+        "breakdown_us": {"step_single_launch": round(step_us, 3), "attention": round(attn_us, 3),
+                         "oproj": round(oproj_us, 3)},
     }
 
     if not args.no_parity or not args.no_cpu_baseline:

@@ -28,6 +28,7 @@ DA_ERR_LAUNCH = -5
 DA_HEAD_DIM = 128
 DA_MAX_GROUP = 16
 DA_FLAG_DEBUG_SCORES = 1
+DA_FLAG_SEPARATE = 2
 
 EXPORTED = (
     "decode_attn_workspace_size",
@@ -196,8 +197,9 @@ class Workspace:
 
 
 def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Optional[Workspace] = None,
-                    softmax_scale: float = 0.0, debug_scores=None, debug_lse=None, stream=None):
-    """One decode step: returns out [B, hidden] bf16."""
+                    softmax_scale: float = 0.0, debug_scores=None, debug_lse=None, stream=None, separate=False):
+    """One decode step: returns out [B, hidden] bf16. ``separate`` asks for two
+    launches (attention, projection) where the plan would use one."""
     torch = _check_dev("q", q, _torch().bfloat16)
     _check_dev("k_cache", k_cache, torch.bfloat16)
     _check_dev("v_cache", v_cache, torch.bfloat16)
@@ -208,7 +210,7 @@ def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace
     hidden = o_weight.shape[1]
     if out is None:
         out = torch.empty((B, hidden), dtype=torch.bfloat16, device=q.device)
-    flags = DA_FLAG_DEBUG_SCORES if debug_scores is not None else 0
+    flags = (DA_FLAG_DEBUG_SCORES if debug_scores is not None else 0) | (DA_FLAG_SEPARATE if separate else 0)
     shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale, flags=flags, debug_scores=_ptr(debug_scores),
                        debug_lse=_ptr(debug_lse))
     need = decode_attn_workspace_size(shape)
@@ -294,10 +296,10 @@ class PreparedCall:
         return self.result
 
 
-def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what):
+def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what, flags=0):
     B, Hq, D = q.shape
     _, Hkv, Lmax, _ = k_cache.shape
-    shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale)
+    shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale, flags=flags)
     need = decode_attn_workspace_size(shape)
     if need == 0:
         raise DecodeAttnError(DA_ERR_SHAPE, what)
@@ -308,7 +310,7 @@ def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what):
 
 
 def DecodeStep(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Optional[Workspace] = None,
-               softmax_scale: float = 0.0, stream=None) -> PreparedCall:
+               softmax_scale: float = 0.0, stream=None, separate=False) -> PreparedCall:
     """A prepared ``decode_attn_fwd``; calling it runs one decode step and returns ``out``."""
     torch = _check_dev("q", q, _torch().bfloat16)
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("o_weight", o_weight)):
@@ -316,7 +318,8 @@ def DecodeStep(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Opt
     _check_dev("seq_lens", seq_lens, torch.int32)
     if out is None:
         out = torch.empty((q.shape[0], o_weight.shape[1]), dtype=torch.bfloat16, device=q.device)
-    shape, ws = _prepare_shape(q, k_cache, o_weight.shape[1], softmax_scale, workspace, "decode_attn_fwd")
+    shape, ws = _prepare_shape(q, k_cache, o_weight.shape[1], softmax_scale, workspace, "decode_attn_fwd",
+                               DA_FLAG_SEPARATE if separate else 0)
     tensors = (q, k_cache, v_cache, seq_lens, o_weight, out)
     args = [ctypes.c_void_p(t.data_ptr()) for t in tensors] + [ctypes.byref(shape),
                                                               ctypes.c_void_p(_stream_handle(stream))]

@@ -123,15 +123,87 @@ AttnPlan plan_attn(const decode_attn_shape_t* s) {
   return ap;
 }
 
+// ---- the single-launch step for small steps (decode_step.hip) ----
+// Used when the whole step is a few dozen MiB or less: the fixed cost of
+// every dependent trip through memory then outweighs the streaming time.
+constexpr size_t kStepMaxKvBytes = 64ull << 20;
+constexpr size_t kStepMaxWeightBytes = 64ull << 20;
+constexpr int kStepMaxBatch = 4;          // projection rows held per lane
+constexpr int kStepResident = 512;        // workgroups resident at once: two 256-thread ones per CU
+constexpr int kStepAttnTarget = 128;      // attention workgroups aimed at
+constexpr int kStepMaxAttn = 384;         // at most, leaving room for the projection
+constexpr int kPieceGrain = 128;          // keys of a piece: a multiple of 4 waves x 32 keys
+constexpr uint32_t kStepWeightDelay = 0;  // 100 MHz ticks before the projection requests its weight
+constexpr uint32_t kStepStageGap = 0;     // ticks between the 8 stages of those requests
+
+struct StepPlan {
+  bool ok;
+  int gpad, mpad;
+  int pieces, piece_keys, attn_wgs;
+  int tile_n, chunk, tiles, chunks;
+  size_t part_o_bytes, part_ml_bytes, proj_part_bytes;
+};
+
+StepPlan plan_step(const decode_attn_shape_t* s) {
+  StepPlan sp{};
+  const int B = s->batch, Hkv = s->num_kv_heads, G = s->num_q_heads / s->num_kv_heads;
+  const int K = s->num_q_heads * kHeadDim, N = s->hidden;
+  if (B > kStepMaxBatch || (s->flags & DA_FLAG_DEBUG_SCORES)) return sp;
+  if ((size_t)B * Hkv * s->max_seq_len * kHeadDim * 4 > kStepMaxKvBytes) return sp;
+  if ((size_t)K * N * 2 > kStepMaxWeightBytes) return sp;
+  sp.gpad = pow2_at_least(G);
+  sp.mpad = pow2_at_least(B);
+  const int seqs = B * Hkv;
+  const int grains = ceil_div(s->max_seq_len, kPieceGrain);
+  int pieces = std::min(grains, std::max(1, ceil_div(kStepAttnTarget, seqs)));
+  sp.piece_keys = kPieceGrain * ceil_div(grains, pieces);
+  sp.pieces = ceil_div(s->max_seq_len, sp.piece_keys);
+  sp.attn_wgs = seqs * sp.pieces;
+  if (sp.attn_wgs > kStepMaxAttn) return sp;
+  // projection: a tile of tile_n columns x a K-chunk of 16384 / tile_n rows per
+  // workgroup; every column tile merges the attention pieces of its chunk, so
+  // the choice with the fewest bytes of merge reads and K-chunk partials wins
+  const size_t part_o = (size_t)sp.attn_wgs * G * kHeadDim * sizeof(float);
+  size_t best_cost = ~(size_t)0;
+  int best = 0;
+  for (int tc : {512, 256, 128}) {
+    const int kc = da::decode_step_chunk(tc), nh = kc / kHeadDim;
+    if (K % kc != 0 || (nh % G != 0 && G % nh != 0)) continue;
+    if (!da::decode_step_supported(sp.gpad, sp.mpad, tc)) continue;
+    const int tiles = ceil_div(N, tc), chunks = K / kc;
+    const int wgs = tiles * chunks;
+    if (sp.attn_wgs + wgs > kStepResident) continue;
+    const size_t cost = (size_t)tiles * part_o + (chunks > 1 ? 2ull * chunks * B * N * sizeof(float) : 0);
+    if (cost > best_cost || (cost == best_cost && wgs <= best)) continue;
+    best_cost = cost;
+    best = wgs;
+    sp.tile_n = tc;
+    sp.chunk = kc;
+    sp.tiles = tiles;
+    sp.chunks = chunks;
+  }
+  if (best == 0) return sp;
+  sp.part_o_bytes = align_up((size_t)sp.attn_wgs * G * kHeadDim * sizeof(float), kAlign);
+  sp.part_ml_bytes = align_up((size_t)sp.attn_wgs * G * 2 * sizeof(float), kAlign);
+  sp.proj_part_bytes = sp.chunks > 1 ? align_up((size_t)sp.chunks * B * N * sizeof(float), kAlign) : 0;
+  sp.ok = (seqs * da::kStepReplicas + sp.tiles) * da::kCounterStride <= da::kStepCounterBase;
+  return sp;
+}
+
 struct Layout {
   AttnPlan attn;
   ProjPlan proj;
+  StepPlan step;
   size_t off_part_o, off_part_ml, off_flat, off_proj_part, total;
   int attn_counter0, proj_counter0;
   bool fits;
+  bool fused;  // decode_attn_fwd runs the single-launch step
 };
 
 // Workspace: [arrival counters][attention partials][attention output][projection partials]
+// for two launches; the single-launch step lays [piece partials][projection
+// partials] over the same bytes after the counters. Both are reserved, so the
+// size does not depend on the flags.
 Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
   Layout L{};
   L.attn = plan_attn(s);
@@ -142,6 +214,7 @@ Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
   off += L.attn.part_ml_bytes;
   L.attn_counter0 = 0;
   int counters = s->batch * s->num_kv_heads;
+  L.fused = false;
   if (with_proj) {
     L.proj = plan_proj(s->batch, s->num_q_heads * kHeadDim, s->hidden);
     L.off_flat = off;
@@ -150,9 +223,16 @@ Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
     off += L.proj.part_bytes;
     L.proj_counter0 = counters;
     counters += L.proj.tiles;
+    L.step = plan_step(s);
+    if (L.step.ok) {
+      const size_t step_total =
+          da::kCounterBlockBytes + L.step.part_o_bytes + L.step.part_ml_bytes + L.step.proj_part_bytes;
+      off = std::max(off, step_total);
+      L.fused = !(s->flags & DA_FLAG_SEPARATE);
+    }
   }
   L.total = off;
-  L.fits = counters <= da::kMaxCounters && L.attn.part_o_bytes < (1ull << 32);
+  L.fits = counters <= da::kStepCounterBase && L.attn.part_o_bytes < (1ull << 32);
   return L;
 }
 
@@ -210,22 +290,28 @@ int run_attention(const da::AttnParams& p, const Layout& L, hipStream_t st) {
   return da::launch_attention(p, L.attn.gpad, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
+da::GemvParams gemv_params(const ProjPlan& pp, const void* x, const void* w, void* out, int M, int K, int N,
+                           char* part, char* cnt) {
+  da::GemvParams g{};
+  g.x = (const uint16_t*)x;
+  g.w = (const uint16_t*)w;
+  g.out = (uint16_t*)out;
+  g.part = (float*)part;
+  g.counters = (uint32_t*)cnt;
+  g.M = M;
+  g.K = K;
+  g.N = N;
+  g.kchunk = pp.kchunk;
+  g.ksplit = pp.ksplit;
+  g.tile_n = pp.tile_n;
+  g.part_bytes = (uint32_t)std::min<size_t>(pp.part_bytes, 0xffffffffu);
+  return g;
+}
+
 int run_proj(const ProjPlan& pp, const void* x, const void* w, void* out, int M, int K, int N, char* part,
              char* cnt, hipStream_t st) {
   if (pp.path == 0) {
-    da::GemvParams g{};
-    g.x = (const uint16_t*)x;
-    g.w = (const uint16_t*)w;
-    g.out = (uint16_t*)out;
-    g.part = (float*)part;
-    g.counters = (uint32_t*)cnt;
-    g.M = M;
-    g.K = K;
-    g.N = N;
-    g.kchunk = pp.kchunk;
-    g.ksplit = pp.ksplit;
-    g.tile_n = pp.tile_n;
-    g.part_bytes = (uint32_t)std::min<size_t>(pp.part_bytes, 0xffffffffu);
+    const da::GemvParams g = gemv_params(pp, x, w, out, M, K, N, part, cnt);
     return da::launch_gemv(g, pp.mpad, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
   }
   da::GemmParams g{};
@@ -241,6 +327,48 @@ int run_proj(const ProjPlan& pp, const void* x, const void* w, void* out, int M,
   g.ksplit = pp.ksplit;
   g.part_bytes = (uint32_t)std::min<size_t>(pp.part_bytes, 0xffffffffu);
   return da::launch_gemm_bf16(g, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+int run_step(const void* q, const void* k, const void* v, const int32_t* sl, const void* w, void* out,
+             const decode_attn_shape_t* s, const Layout& L, hipStream_t st) {
+  const StepPlan& sp = L.step;
+  char* ws = (char*)s->workspace;
+  uint32_t* cnt = (uint32_t*)ws;
+  da::StepParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.seq_lens = sl;
+  p.w = (const uint16_t*)w;
+  p.out = (uint16_t*)out;
+  char* data = ws + da::kCounterBlockBytes;
+  p.part_o = (float*)data;
+  p.part_ml = (float*)(data + sp.part_o_bytes);
+  p.proj_part = (float*)(data + sp.part_o_bytes + sp.part_ml_bytes);
+  p.part_o_bytes = (uint32_t)sp.part_o_bytes;
+  p.part_ml_bytes = (uint32_t)sp.part_ml_bytes;
+  p.proj_part_bytes = (uint32_t)sp.proj_part_bytes;
+  p.seq_cnt = cnt;
+  p.proj_cnt = cnt + s->batch * s->num_kv_heads * da::kStepReplicas * da::kCounterStride;
+  p.pass_top = cnt + da::kStepCounterBase;
+  p.error = cnt + da::kStepCounterBase + 1;
+  p.pass_sub = cnt + da::kStepCounterBase + 32;
+  p.B = s->batch;
+  p.Hq = s->num_q_heads;
+  p.Hkv = s->num_kv_heads;
+  p.G = s->num_q_heads / s->num_kv_heads;
+  p.Lmax = s->max_seq_len;
+  p.N = s->hidden;
+  p.piece_keys = sp.piece_keys;
+  p.pieces = sp.pieces;
+  p.attn_wgs = sp.attn_wgs;
+  p.tiles = sp.tiles;
+  p.chunks = sp.chunks;
+  p.weight_delay = kStepWeightDelay;
+  p.stage_gap = kStepStageGap;
+  const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return da::launch_decode_step(p, sp.gpad, sp.mpad, sp.tile_n, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -261,6 +389,20 @@ int decode_attn_plan(const decode_attn_shape_t* shape, decode_attn_plan_t* plan)
   const int G = shape->num_q_heads / shape->num_kv_heads;
   const int Ko = shape->num_q_heads * kHeadDim;
   memset(plan, 0, sizeof *plan);
+  if (L.fused) {
+    // one launch: a fixed number of pieces per sequence, projection tiles of whole kv heads
+    const StepPlan& sp = L.step;
+    const int wgs = sp.attn_wgs;
+    plan->qk = {G, kHeadDim, shape->max_seq_len, 16, kHeadDim, kAttnBlockKeys, sp.pieces, wgs};
+    plan->pv = {G, shape->max_seq_len, kHeadDim, sp.gpad, kAttnBlockKeys, kHeadDim, sp.pieces, wgs};
+    plan->oproj = {shape->batch, Ko, shape->hidden, sp.mpad, sp.chunk, sp.tile_n, sp.chunks, sp.tiles * sp.chunks};
+    plan->split_len = sp.piece_keys;
+    plan->num_splits = sp.pieces;
+    plan->oproj_path = 0;
+    plan->fused = 1;
+    plan->workspace_bytes = L.total;
+    return DA_OK;
+  }
   const int wgs = L.attn.workgroups;
   // QK^T per kv head: M = G, K = head_dim (whole), N = keys (32 per wave step)
   plan->qk = {G, kHeadDim, shape->max_seq_len, 16, kHeadDim, kAttnBlockKeys, wgs, wgs};
@@ -292,6 +434,7 @@ int decode_attn_fwd(const void* q, const void* k_cache, const void* v_cache, con
   char* ws = (char*)shape->workspace;
   void* flat = ws + L.off_flat;
   const da::AttnParams p = attn_params(q, k_cache, v_cache, seq_lens, flat, shape, L);
+  if (L.fused) return run_step(q, k_cache, v_cache, seq_lens, o_weight, out, shape, L, st);
   if ((rc = run_attention(p, L, st))) return rc;
   return run_proj(L.proj, flat, o_weight, out, shape->batch, shape->num_q_heads * kHeadDim, shape->hidden,
                   ws + L.off_proj_part, (char*)((uint32_t*)ws + L.proj_counter0), st);

@@ -227,30 +227,28 @@ __device__ __forceinline__ void attn_block(AttnWave<GP>& w, const KVTile<KB>& t,
   wave_lds_fence();
 }
 
-// The wave's steps first, first+step, ... (n of them, KB keys each), with the
-// loads of the next step in flight while the current one is computed.
-template <int GP, int KB>
+// The wave's steps first, first+step, ... (n of them, KB keys each). The loads
+// of the next D-1 steps are in flight while a step is computed (D register
+// sets, indexed statically through the unrolled inner loop).
+template <int GP, int KB, int D>
 __device__ __forceinline__ void attn_wave_steps(AttnWave<GP>& w, const uint4 (&qa)[4], const AttnSeg& sg, int first,
                                                 int step, int n, int end, float* sp, int col, int grp) {
   if (n <= 0) return;
-  KVTile<KB> ta, tb;
-  load_kv<KB>(ta, sg, first * KB, col, grp);
-  int i = 0;
-  while (true) {
-    if (i + 1 < n) load_kv<KB>(tb, sg, (first + (i + 1) * step) * KB, col, grp);
-    attn_block<GP, KB>(w, ta, qa, sg, (first + i * step) * KB, end, sp, col, grp);
-    if (++i >= n) break;
-    if (i + 1 < n) load_kv<KB>(ta, sg, (first + (i + 1) * step) * KB, col, grp);
-    attn_block<GP, KB>(w, tb, qa, sg, (first + i * step) * KB, end, sp, col, grp);
-    if (++i >= n) break;
+  KVTile<KB> t[D];
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j)
+    if (j < n) load_kv<KB>(t[j], sg, (first + j * step) * KB, col, grp);
+  for (int i0 = 0; i0 < n; i0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      if (i < n) {
+        if (i + D - 1 < n) load_kv<KB>(t[(j + D - 1) % D], sg, (first + (i + D - 1) * step) * KB, col, grp);
+        attn_block<GP, KB>(w, t[j], qa, sg, (first + i * step) * KB, end, sp, col, grp);
+      }
+    }
   }
 }
-
-// Keys per wave step for a padded group size.
-template <int GP>
-struct StepKeys {
-  static constexpr int value = GP >= 8 ? 16 : 32;
-};
 
 // Reduce the wave's state (row sums of l over the 16 key lanes, O over the 4
 // key groups) and park it in LDS: so[g][128], sm[g], sl[g].

@@ -1,0 +1,230 @@
+// The stream-K attention of one workgroup.
+//
+// The keys of all (batch, kv head) sequences are laid end to end as 32-key
+// blocks: sequence (b, h) owns ceil(L_b / 32) consecutive blocks, b-major. The
+// T blocks are cut into W equal contiguous ranges, one per workgroup, so ragged
+// and uniform batches alike give every workgroup the same number of bytes to
+// stream. A workgroup walks its range sequence by sequence; its waves take
+// interleaved steps of the piece it is on (attn_core.hpp). A piece that is a
+// whole sequence is normalised and written as bf16 at once; otherwise its
+// un-normalised partial (O, running max, weight sum) goes to a workspace slot
+// through device-coherent stores, and the last workgroup to finish a piece of
+// that sequence (an arrival counter per sequence tells it) merges all of its
+// pieces and writes the bf16 output.
+#pragma once
+
+#include "attn_core.hpp"
+#include "kernels.hpp"
+
+namespace da {
+
+constexpr int kMergeBatch = 16;  // partials whose loads are in flight together in the merge
+
+// Block range [bound(i), bound(i+1)) of workgroup i of W over T blocks, and the
+// workgroup that owns block x. With T < W the first T workgroups take one
+// block each and the rest none.
+__device__ __forceinline__ long range_bound(long i, long T, long W) { return T >= W ? (i * T) / W : (i < T ? i : T); }
+__device__ __forceinline__ long range_owner(long x, long T, long W) { return T >= W ? ((x + 1) * W - 1) / T : x; }
+
+// One workgroup's share of the stream-K attention: workgroup `wg` of `W`.
+template <int GP, int NW, int KB, int D>
+__device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, long W) {
+  constexpr int NT = NW * kWave;
+  __shared__ int s_pre[kMaxAttnBatch + 1];  // blocks of the sequences before batch b (per kv head)
+  __shared__ int s_len[kMaxAttnBatch];
+  __shared__ int s_scan[NT];
+  __shared__ float s_p[NW][KB * GP];
+  __shared__ float s_o[NW][GP][kHeadDim];
+  __shared__ float s_m[NW][GP], s_l[NW][GP];
+  __shared__ float s_cm[NT], s_cl[NT];
+  __shared__ float4 s_co[NT];
+
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int B = p.B, Hkv = p.Hkv, G = p.G;
+  DA_TRACE(0);
+
+  // ---- blocks per sequence and their prefix sums (one scan per workgroup) ----
+  const int per = (B + NT - 1) / NT;
+  int local = 0;
+  for (int j = 0; j < per; ++j) {
+    const int b = t * per + j;
+    if (b < B) {
+      const int L = min(max(p.seq_lens[b], 0), p.Lmax);
+      s_len[b] = L;
+      local += (L + kBlockKeys - 1) / kBlockKeys;
+    }
+  }
+  s_scan[t] = local;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const int v = t >= off ? s_scan[t - off] : 0;
+    __syncthreads();
+    s_scan[t] += v;
+    __syncthreads();
+  }
+  {
+    int run = s_scan[t] - local;
+    for (int j = 0; j < per; ++j) {
+      const int b = t * per + j;
+      if (b < B) {
+        s_pre[b] = run;
+        run += (s_len[b] + kBlockKeys - 1) / kBlockKeys;
+      }
+    }
+    if (t == 0) s_pre[B] = s_scan[NT - 1];
+  }
+  __syncthreads();
+
+  DA_TRACE(1);
+  const long T = (long)Hkv * s_pre[B];
+  long x = range_bound(wg, T, W);
+  const long xe = range_bound(wg + 1, T, W);
+  const rsrc_t part_o = make_rsrc(p.part_o, p.part_o_bytes);
+  const rsrc_t part_ml = make_rsrc(p.part_ml, p.part_ml_bytes);
+  // the bf16 output of 4 dims
+  auto store4 = [&](int b, int qh, int d4, const float (&o)[4], float inv) {
+    const uint32_t w01 = (uint32_t)f32_to_bf16_rne(o[0] * inv) | ((uint32_t)f32_to_bf16_rne(o[1] * inv) << 16);
+    const uint32_t w23 = (uint32_t)f32_to_bf16_rne(o[2] * inv) | ((uint32_t)f32_to_bf16_rne(o[3] * inv) << 16);
+    *reinterpret_cast<uint2*>(p.flat + ((size_t)b * p.Hq + qh) * kHeadDim + d4 * 4) = make_uint2(w01, w23);
+  };
+
+  while (x < xe) {
+    // ---- the sequence (b, h) that block x belongs to ----
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((long)Hkv * s_pre[mid] <= x) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int nb = s_pre[b + 1] - s_pre[b];
+    const long seg0 = (long)Hkv * s_pre[b];
+    const int h = (int)((x - seg0) / nb);
+    const long ss = seg0 + (long)h * nb, se = ss + nb;
+    const long pe = min(xe, se);
+    const int lb0 = (int)(x - ss), lb1 = (int)(pe - ss);
+    const bool whole = (x == ss && pe == se);
+    const int seg = b * Hkv + h;
+    const int L = s_len[b];
+
+    AttnSeg sg;
+    const size_t kv_off = (size_t)seg * p.Lmax * kHeadDim;
+    sg.K = make_rsrc(p.k + kv_off, (uint32_t)L * kRowBytes);
+    sg.V = make_rsrc(p.v + kv_off, (uint32_t)L * kRowBytes);
+    sg.L = L;
+    sg.G = G;
+    sg.scale_log2 = p.scale_log2;
+    sg.scale = p.scale;
+    sg.dbg = p.dbg_scores ? p.dbg_scores + ((size_t)b * p.Hq + (size_t)h * G) * p.Lmax : nullptr;
+    sg.dbg_stride = p.Lmax;
+
+    uint4 qa[4];
+    load_query(qa, p.q + ((size_t)b * p.Hq + (size_t)h * G) * kHeadDim, G, col, grp);
+    AttnWave<GP> aw;
+    aw.reset();
+    // the piece's keys [lb0*32, min(lb1*32, L)) in steps of KB keys, interleaved over the
+    // waves; every step holds at least one key of the sequence
+    constexpr int SPB = kBlockKeys / KB;  // steps per block
+    const int nstep = (min(lb1 * kBlockKeys, L) - lb0 * kBlockKeys + KB - 1) / KB;
+    const int n = nstep > wave ? (nstep - wave + NW - 1) / NW : 0;
+    attn_wave_steps<GP, KB, D>(aw, qa, sg, lb0 * SPB + wave, NW, n, L, s_p[wave], col, grp);
+    attn_wave_to_lds<GP>(aw, s_o[wave], s_m[wave], s_l[wave], col, grp);
+    __syncthreads();
+    DA_TRACE(2);
+
+    // ---- merge the waves: the whole sequence, or one partial of it ----
+    const int slot = seg + (int)wg;
+    for (int idx = t; idx < G * 32; idx += NT) {
+      const int g = idx >> 5, d4 = idx & 31;
+      float M = s_m[0][g];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+      float Ls = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = exp2f(s_m[w][g] - M);
+        Ls = fmaf(f, s_l[w][g], Ls);
+        const float4 o4 = *reinterpret_cast<const float4*>(&s_o[w][g][d4 * 4]);
+        O[0] = fmaf(f, o4.x, O[0]);
+        O[1] = fmaf(f, o4.y, O[1]);
+        O[2] = fmaf(f, o4.z, O[2]);
+        O[3] = fmaf(f, o4.w, O[3]);
+      }
+      const int qh = h * G + g;
+      if (whole) {
+        store4(b, qh, d4, O, 1.f / Ls);
+        if (p.dbg_lse && d4 == 0) p.dbg_lse[(size_t)b * p.Hq + qh] = (M + log2f(Ls)) * kLn2;
+      } else {
+        const uint32_t so = ((uint32_t)(slot * G + g) * kHeadDim + d4 * 4) * 4;
+        rsrc_st16_coherent(part_o, so, make_uint4(__builtin_bit_cast(uint32_t, O[0]), __builtin_bit_cast(uint32_t, O[1]),
+                                                  __builtin_bit_cast(uint32_t, O[2]), __builtin_bit_cast(uint32_t, O[3])));
+        if (d4 == 0)
+          rsrc_st8_coherent(part_ml, (uint32_t)(slot * G + g) * 8,
+                            make_uint2(__builtin_bit_cast(uint32_t, M), __builtin_bit_cast(uint32_t, Ls)));
+      }
+    }
+
+    if (!whole) {
+      const long first = range_owner(ss, T, W), last = range_owner(se - 1, T, W);
+      const int P = (int)(last - first + 1);
+      const bool last_piece = arrive_last_coherent(&p.counters[seg], (uint32_t)P);
+      DA_TRACE(3);
+      if (last_piece) {
+        // ---- the last piece merges the P partials at slots seg+first .. seg+last ----
+        const int slot0 = seg + (int)first;
+        const int npairs = G * 32;
+        for (int base = 0; base < npairs; base += NT) {
+          const int cnt = min(npairs - base, NT);
+          const int nph = NT / cnt;
+          const int pr = base + t % cnt, ph = t / cnt;
+          float M = -INFINITY, Ls = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
+          if (ph < nph) {
+            const int g = pr >> 5, d4 = pr & 31;
+            for (int j0 = ph; j0 < P; j0 += kMergeBatch * nph) {
+              uint2 ml[kMergeBatch];
+              uint4 ov[kMergeBatch];
+#pragma unroll
+              for (int u = 0; u < kMergeBatch; ++u) {
+                const int j = j0 + u * nph;
+                const uint32_t sl = (uint32_t)((slot0 + min(j, P - 1)) * G + g);
+                ml[u] = rsrc_ld8_coherent(part_ml, sl * 8);
+                ov[u] = rsrc_ld16_coherent(part_o, (sl * kHeadDim + d4 * 4) * 4);
+              }
+#pragma unroll
+              for (int u = 0; u < kMergeBatch; ++u) {
+                if (j0 + u * nph < P) {
+                  const float o[4] = {__builtin_bit_cast(float, ov[u].x), __builtin_bit_cast(float, ov[u].y),
+                                      __builtin_bit_cast(float, ov[u].z), __builtin_bit_cast(float, ov[u].w)};
+                  merge_partial(M, Ls, O, __builtin_bit_cast(float, ml[u].x), __builtin_bit_cast(float, ml[u].y), o);
+                }
+              }
+            }
+          }
+          s_cm[t] = M;
+          s_cl[t] = Ls;
+          s_co[t] = make_float4(O[0], O[1], O[2], O[3]);
+          __syncthreads();
+          if (t < cnt) {
+            float Mf = -INFINITY, Lf = 0.f, Of[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int q2 = 0; q2 < nph; ++q2) {
+              const float4 o4 = s_co[t + q2 * cnt];
+              const float o[4] = {o4.x, o4.y, o4.z, o4.w};
+              merge_partial(Mf, Lf, Of, s_cm[t + q2 * cnt], s_cl[t + q2 * cnt], o);
+            }
+            const int g = pr >> 5, d4 = pr & 31;
+            const int qh = h * G + g;
+            store4(b, qh, d4, Of, 1.f / Lf);
+            if (p.dbg_lse && d4 == 0) p.dbg_lse[(size_t)b * p.Hq + qh] = (Mf + log2f(Lf)) * kLn2;
+          }
+          __syncthreads();
+        }
+        DA_TRACE(4);
+      }
+    }
+    __syncthreads();  // LDS is reused by the next piece
+    x = pe;
+  }
+  DA_TRACE(6);
+}
+
+}  // namespace da

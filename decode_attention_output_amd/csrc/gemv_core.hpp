@@ -1,0 +1,119 @@
+// GEMV building blocks shared by the projection kernel and the single-launch
+// decode step: out[M, N] = x[M, K] @ w[K, N] for M < 16 on the vector ALUs.
+#pragma once
+
+#include "attn_core.hpp"
+#include "kernels.hpp"
+
+namespace da {
+
+constexpr int kGemvThreads = 256;
+
+// The end of a GEMV workgroup: reduce the per-lane sums of a TC-column tile
+// (row lanes of a wave by shuffles, the 4 waves in LDS), then write bf16 when
+// the K axis is not split, or store the fp32 partial through device-coherent
+// stores; the last K-chunk of the tile to arrive adds all partials in chunk
+// order (deterministic) and writes bf16. `counter` is the tile's arrival counter.
+template <int MB, int TC>
+__device__ __forceinline__ void gemv_finish(const GemvParams& p, float (&acc)[MB][8], int tile, int ks,
+                                            uint32_t* counter) {
+  constexpr int kStrip = TC;
+  constexpr int kLanesPerRow = TC / 8;
+  __shared__ float s_red[kGemvThreads / kWave][MB][kStrip];
+  __shared__ float4 s_fin[kGemvThreads];
+  const int t = threadIdx.x;
+  const int n0 = tile * kStrip;
+  // reduce the row lanes of a wave (lanes l, l^LPR, l^2LPR, ...), then the 4 waves
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[m][e];
+#pragma unroll
+      for (int x = kLanesPerRow; x < kWave; x <<= 1) v += __shfl_xor(v, x);
+      acc[m][e] = v;
+    }
+  const int wave = t / kWave, lane = t % kWave;
+  if (lane < kLanesPerRow) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      *reinterpret_cast<float4*>(&s_red[wave][m][lane * 8]) = make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
+      *reinterpret_cast<float4*>(&s_red[wave][m][lane * 8 + 4]) =
+          make_float4(acc[m][4], acc[m][5], acc[m][6], acc[m][7]);
+    }
+  }
+  __syncthreads();
+
+  // 16 groups of 4 columns per activation row
+  const int M = p.M;
+  const int npairs = M * (kStrip / 4);
+  const rsrc_t part = make_rsrc(p.part, p.part_bytes);
+  for (int pr = t; pr < npairs; pr += kGemvThreads) {
+    const int m = pr / (kStrip / 4), c4 = pr % (kStrip / 4);
+    float4 v = *reinterpret_cast<const float4*>(&s_red[0][m][c4 * 4]);
+#pragma unroll
+    for (int w = 1; w < kGemvThreads / kWave; ++w) {
+      const float4 o = *reinterpret_cast<const float4*>(&s_red[w][m][c4 * 4]);
+      v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+    }
+    const int col = n0 + c4 * 4;
+    if (col >= p.N) continue;
+    if (p.ksplit == 1) {
+      const uint32_t w01 = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+      const uint32_t w23 = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+      *reinterpret_cast<uint2*>(p.out + (size_t)m * p.N + col) = make_uint2(w01, w23);
+    } else {
+      rsrc_st16_coherent(part, (uint32_t)((((size_t)ks * M + m) * p.N + col) * 4),
+                         make_uint4(__builtin_bit_cast(uint32_t, v.x), __builtin_bit_cast(uint32_t, v.y),
+                                    __builtin_bit_cast(uint32_t, v.z), __builtin_bit_cast(uint32_t, v.w)));
+    }
+  }
+  if (p.ksplit == 1) return;
+  if (!arrive_last_coherent(counter, (uint32_t)p.ksplit)) return;
+  DA_TRACE(13);
+
+  // last K-chunk of the strip: add the partials of all chunks, in chunk order per phase
+  for (int base = 0; base < npairs; base += kGemvThreads) {
+    const int cnt = min(npairs - base, kGemvThreads);
+    const int nph = kGemvThreads / cnt;
+    const int pr = base + t % cnt, ph = t / cnt;
+    const int m = pr / (kStrip / 4), c4 = pr % (kStrip / 4);
+    const int col = n0 + c4 * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ph < nph && col < p.N) {
+      for (int s0 = ph; s0 < p.ksplit; s0 += 16 * nph) {
+        uint4 pv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int sidx = min(s0 + u * nph, p.ksplit - 1);
+          pv[u] = rsrc_ld16_coherent(part, (uint32_t)((((size_t)sidx * M + m) * p.N + col) * 4));
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (s0 + u * nph < p.ksplit) {
+            v.x += __builtin_bit_cast(float, pv[u].x);
+            v.y += __builtin_bit_cast(float, pv[u].y);
+            v.z += __builtin_bit_cast(float, pv[u].z);
+            v.w += __builtin_bit_cast(float, pv[u].w);
+          }
+        }
+      }
+    }
+    s_fin[t] = v;
+    __syncthreads();
+    if (t < cnt && col < p.N) {
+      float4 f = s_fin[t];
+      for (int q2 = 1; q2 < nph; ++q2) {
+        const float4 o = s_fin[t + q2 * cnt];
+        f.x += o.x; f.y += o.y; f.z += o.z; f.w += o.w;
+      }
+      const uint32_t w01 = (uint32_t)f32_to_bf16_rne(f.x) | ((uint32_t)f32_to_bf16_rne(f.y) << 16);
+      const uint32_t w23 = (uint32_t)f32_to_bf16_rne(f.z) | ((uint32_t)f32_to_bf16_rne(f.w) << 16);
+      *reinterpret_cast<uint2*>(p.out + (size_t)m * p.N + col) = make_uint2(w01, w23);
+    }
+    __syncthreads();
+  }
+}
+
+
+}  // namespace da

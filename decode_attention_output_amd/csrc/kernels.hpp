@@ -5,6 +5,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Timeline hook: thread 0 of a workgroup may record a timestamp at numbered
+// points of the kernels. It expands to nothing unless a build defines it.
+#ifndef DA_TRACE
+#define DA_TRACE(point) ((void)0)
+#endif
+
 namespace da {
 
 // Every workspace starts with a block of arrival counters that are zero
@@ -30,6 +36,7 @@ struct AttnParams {
   float* dbg_lse;           // optional fp32 [B, Hq]
   int B, Hq, Hkv, G, Lmax;
   int num_workgroups;       // stream-K workgroups; slots = num_workgroups + B * Hkv
+  int step_variant;         // 0: default step shape for the group size; 1..4: (32,2) (16,2) (16,3) (16,4)
   float scale;       // softmax scale (natural units)
   float scale_log2;  // scale * log2(e)
 };
@@ -60,6 +67,52 @@ struct GemmParams {
 };
 
 hipError_t launch_attention(const AttnParams& p, int gpad, hipStream_t s);
+// The single-launch decode step for small steps (a few tokens, a few thousand
+// cached keys): attention workgroups, one per fixed piece of every (batch, kv
+// head) sequence, followed in the same grid by projection workgroups that
+// merge the pieces of the heads they need and multiply.
+struct StepParams {
+  const uint16_t* q;        // bf16 [B, Hq, 128]
+  const uint16_t* k;        // bf16 [B, Hkv, Lmax, 128]
+  const uint16_t* v;        // bf16 [B, Hkv, Lmax, 128]
+  const int32_t* seq_lens;  // [B]
+  const uint16_t* w;        // bf16 [Hq*128, N]
+  uint16_t* out;            // bf16 [B, N]
+  float* part_o;            // fp32 [B*Hkv*pieces, G, 128] un-normalised piece outputs
+  float* part_ml;           // fp32 [B*Hkv*pieces, G, 2]   (max in log2 units, weight sum)
+  float* proj_part;         // fp32 [chunks, B, N] (chunks > 1)
+  uint32_t part_o_bytes, part_ml_bytes, proj_part_bytes;
+  uint32_t* seq_cnt;        // pieces stored per sequence, kStepReplicas copies, one per 128-byte line
+  uint32_t* proj_cnt;       // arrival counters of the K-chunks per column tile (chunks > 1), one per line
+  uint32_t* pass_sub;       // [32] projection workgroups past their wait, by index mod 32
+  uint32_t* pass_top;       // groups of pass_sub that are complete
+  uint32_t* error;          // set to 1 when a projection workgroup stopped waiting
+  int B, Hq, Hkv, G, Lmax, N;
+  int piece_keys, pieces;   // keys per piece (a multiple of 128), pieces per sequence
+  int attn_wgs;             // B * Hkv * pieces
+  int tiles, chunks;        // projection: column tiles x K-chunks (query heads of one kv head or whole kv heads)
+  uint32_t weight_delay;    // 100 MHz ticks a projection workgroup waits before its first weight loads
+  uint32_t stage_gap;       // ticks between its 8 stages of weight loads
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+// Counters of the single-launch step that many workgroups poll or update sit
+// one per 128-byte line (accesses to one line are serialised), and every
+// sequence's piece count is kept kStepReplicas times, so that each copy has
+// only a few pollers: seq_cnt[(seq * kStepReplicas + copy) * kCounterStride].
+constexpr int kCounterStride = 32;
+constexpr int kStepReplicas = 4;
+
+// Fixed slots of the counter block used by the single-launch step.
+constexpr int kStepCounterBase = kMaxCounters - 64;  // pass_top, error, then pass_sub[32] at +32
+
+// Shapes the single-launch step is built for: query group (padded), batch rows
+// (padded) and tile_n output columns per projection workgroup, whose K-chunk
+// is then 32 rows per lane: 16384 / tile_n rows.
+bool decode_step_supported(int gpad, int mpad, int tile_n);
+int decode_step_chunk(int tile_n);
+hipError_t launch_decode_step(const StepParams& p, int gpad, int mpad, int tile_n, hipStream_t s);
+
 hipError_t launch_gemv(const GemvParams& p, int mpad, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_f16(const GemmParams& p, hipStream_t s);

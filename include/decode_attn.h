@@ -54,6 +54,8 @@ extern "C" {
 
 /* flags */
 #define DA_FLAG_DEBUG_SCORES 1u /* also write debug_scores / debug_lse (test use) */
+#define DA_FLAG_SEPARATE 2u     /* decode_attn_fwd: attention and projection as two
+                                   launches even where the plan would fuse them */
 
 /*
  * Shape and per-call options of one decode step. All sizes in elements.
@@ -114,7 +116,9 @@ typedef struct {
   int32_t split_len;    /* keys per attention workgroup (flash-decoding split)       */
   int32_t num_splits;   /* ceil(max_seq_len / split_len)                              */
   int32_t oproj_path;   /* 0: VALU GEMV (B < 16), 1: MFMA GEMM (B >= 16)             */
-  int32_t fused;        /* 1: the whole step runs as one cooperative launch           */
+  int32_t fused;        /* 1: decode_attn_fwd runs the step as one launch (small
+                           steps, B < 16): projection workgroups stream their weight
+                           tile while the attention runs, then wait for it          */
   size_t workspace_bytes;
 } decode_attn_plan_t;
 

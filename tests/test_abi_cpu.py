@@ -140,13 +140,42 @@ def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
     # the long axis (keys) is streamed 32 keys per wave step and cut evenly over the workgroups
     assert plan.qk.tile_n == 32 and plan.pv.tile_k == 32
     keys = cfg["batch"] * cfg["num_kv_heads"] * cfg["max_seq_len"]
-    assert plan.split_len % 32 == 0 and plan.split_len * plan.num_splits >= keys
-    assert plan.split_len * (plan.num_splits - 1) < keys + 32 * plan.num_splits
-    # the keys are spread over enough workgroups for the 256 compute units when the problem allows
-    # it, but never so many that a workgroup streams fewer than 128 keys
-    assert plan.qk.workgroups >= min(256, keys // 128)
-    assert plan.split_len >= min(128, 32 * (-(-keys // 32)))
-    assert plan.oproj.workgroups >= min(256, (cfg["hidden"] // 64) * (cfg["num_q_heads"] * 128 // 256))
+    if plan.fused:
+        # one launch: every sequence cut into the same pieces of a multiple of 128 keys
+        assert plan.split_len % 128 == 0 and plan.num_splits == -(-cfg["max_seq_len"] // plan.split_len)
+        assert plan.qk.workgroups == cfg["batch"] * cfg["num_kv_heads"] * plan.num_splits
+        assert plan.qk.workgroups >= min(128, keys // 128)
+    else:
+        # stream-K: the keys of all sequences cut into equal ranges, one per workgroup
+        assert plan.split_len % 32 == 0 and plan.split_len * plan.num_splits >= keys
+        assert plan.split_len * (plan.num_splits - 1) < keys + 32 * plan.num_splits
+        # the keys are spread over enough workgroups for the 256 compute units when the problem
+        # allows it, but never so many that a workgroup streams fewer than 128 keys
+        assert plan.qk.workgroups >= min(256, keys // 128)
+        assert plan.split_len >= min(128, 32 * (-(-keys // 32)))
+        assert plan.oproj.workgroups >= min(256, (cfg["hidden"] // 64) * (cfg["num_q_heads"] * 128 // 256))
     # projection path: VALU GEMV below 16 rows, MFMA from 16 rows
     assert plan.oproj_path == (1 if cfg["batch"] >= 16 else 0)
     assert plan.workspace_bytes == da.decode_attn_workspace_size(da.make_shape(**cfg))
+
+
+SMALL = [dict(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=256, hidden=512),
+         dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=2048, hidden=4096),
+         dict(batch=3, num_q_heads=16, num_kv_heads=2, max_seq_len=128, hidden=256)]
+LARGE = [dict(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=8192, hidden=4096),
+         dict(batch=4, num_q_heads=64, num_kv_heads=8, max_seq_len=32768, hidden=8192)]
+
+
+@pytest.mark.parametrize("cfg", SMALL + LARGE)
+def test_plan_fuses_small_steps_only(lib, cfg):
+    plan = da.decode_attn_plan(da.make_shape(**cfg))
+    sep = da.decode_attn_plan(da.make_shape(flags=da.DA_FLAG_SEPARATE, **cfg))
+    assert plan.fused == (1 if cfg in SMALL else 0)
+    assert sep.fused == 0
+    # the workspace does not depend on the launch choice
+    assert plan.workspace_bytes == sep.workspace_bytes
+    assert (sep.qk.workgroups, sep.split_len) == (plan.qk.workgroups, plan.split_len)
+    if plan.fused:
+        # every workgroup of the single launch is resident at once (two per compute unit)
+        assert plan.qk.workgroups + plan.oproj.workgroups <= 512
+        assert plan.oproj_path == 0 and plan.oproj.tile_n in (128, 256, 512)

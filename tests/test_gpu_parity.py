@@ -178,16 +178,58 @@ def test_result_does_not_depend_on_the_split(gpu):
     assert ref is not None
 
 
+def _counter_block_is_clear(ws):
+    torch.cuda.synchronize()
+    assert int(ws.buf[:65536].count_nonzero()) == 0, "arrival counters left non-zero"
+
+
 def test_repeat_calls_are_deterministic_and_reuse_the_workspace(gpu):
     ws = da.Workspace()
     a = workloads.custom_decode_inputs(3, 16, 4, [700, 1, 333], seed=26)
     b = workloads.custom_decode_inputs(1, 4, 1, [4000], hidden=512, seed=27)
     r1 = _run_step(a, ws)
+    _counter_block_is_clear(ws)
     r2 = _run_step(b, ws)   # different shape, same (now dirty) workspace
+    _counter_block_is_clear(ws)
     r3 = _run_step(a, ws)
+    _counter_block_is_clear(ws)
     np.testing.assert_array_equal(r1["out"], r3["out"])
     np.testing.assert_array_equal(r1["flat"], r3["flat"])
     _check_step(b, r2, what="after another shape")
+
+
+# ---- the single-launch step against two launches ---------------------------
+
+FUSED = [
+    # (batch, Hq, Hkv, seq_lens, max_seq_len, hidden)
+    (1, 4, 1, [256], 256, 512),
+    (1, 32, 8, [2048], 2048, 4096),
+    (1, 8, 8, [1], 1, 128),
+    (2, 2, 1, [16, 17], 17, 1032),
+    (3, 16, 2, [5, 37, 100], 128, 256),
+    (4, 8, 2, [255, 256, 257, 1000], 1024, 640),
+    (4, 32, 8, [1000, 17, 600, 999], 1000, 4096),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "B%d_H%d_KV%d_Lmax%d_N%d" % (c[0], c[1], c[2], c[4], c[5]))
+def test_single_launch_step_matches_the_oracle_and_two_launches(gpu, case):
+    B, Hq, Hkv, sl, Lmax, hidden = case
+    assert da.decode_attn_plan(da.make_shape(B, Hq, Hkv, Lmax, hidden)).fused == 1
+    inp = workloads.custom_decode_inputs(B, Hq, Hkv, sl, max_seq_len=Lmax, hidden=hidden, seed=B * 1000 + Hq + hidden)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    s, w = dev_i32(inp["seq_lens"]), dev_bf16(inp["o_weight"])
+    ws = da.Workspace()
+    flat = host_words(da.decode_attn_only(q, k, v, s, workspace=ws))
+    outs = []
+    for separate in (False, True, False, False):
+        outs.append(host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, separate=separate)))
+        _counter_block_is_clear(ws)
+    _check_step(inp, {"flat": flat, "out": outs[0]}, what="single launch")
+    _check_step(inp, {"flat": flat, "out": outs[1]}, what="two launches")
+    # the single launch is deterministic across calls on one workspace
+    np.testing.assert_array_equal(outs[0], outs[2])
+    np.testing.assert_array_equal(outs[0], outs[3])
 
 
 # ---- the projection alone ------------------------------------------------
