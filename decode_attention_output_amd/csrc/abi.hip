@@ -394,7 +394,7 @@ int decode_attn_plan(const decode_attn_shape_t* shape, decode_attn_plan_t* plan)
     const StepPlan& sp = L.step;
     const int wgs = sp.attn_wgs;
     plan->qk = {G, kHeadDim, shape->max_seq_len, 16, kHeadDim, kAttnBlockKeys, sp.pieces, wgs};
-    plan->pv = {G, shape->max_seq_len, kHeadDim, sp.gpad, kAttnBlockKeys, kHeadDim, sp.pieces, wgs};
+    plan->pv = {G, shape->max_seq_len, kHeadDim, 16, kAttnBlockKeys, kHeadDim, sp.pieces, wgs};
     plan->oproj = {shape->batch, Ko, shape->hidden, sp.mpad, sp.chunk, sp.tile_n, sp.chunks, sp.tiles * sp.chunks};
     plan->split_len = sp.piece_keys;
     plan->num_splits = sp.pieces;
@@ -407,7 +407,7 @@ int decode_attn_plan(const decode_attn_shape_t* shape, decode_attn_plan_t* plan)
   // QK^T per kv head: M = G, K = head_dim (whole), N = keys (32 per wave step)
   plan->qk = {G, kHeadDim, shape->max_seq_len, 16, kHeadDim, kAttnBlockKeys, wgs, wgs};
   // attn x V per kv head: M = G, K = keys (32 per wave step), N = head_dim (whole)
-  plan->pv = {G, shape->max_seq_len, kHeadDim, L.attn.gpad, kAttnBlockKeys, kHeadDim, wgs, wgs};
+  plan->pv = {G, shape->max_seq_len, kHeadDim, 16, kAttnBlockKeys, kHeadDim, wgs, wgs};
   plan->oproj = {shape->batch, Ko, shape->hidden, L.proj.mpad, L.proj.kchunk, L.proj.tile_n, L.proj.ksplit,
                  L.proj.tiles * L.proj.ksplit};
   plan->split_len = L.attn.keys_per_wg;

@@ -9,29 +9,28 @@ namespace da {
 
 namespace {
 
-template <int GP, int NW, int KB, int D>
-__global__ __launch_bounds__(NW* kWave, GP >= 16 ? 1 : 2) void attn_streamk_kernel(AttnParams p) {
-  attn_streamk_body<GP, NW, KB, D>(p, blockIdx.x, gridDim.x);
+template <int GP, int NW, int D>
+__global__ __launch_bounds__(NW* kWave, 2) void attn_streamk_kernel(AttnParams p) {
+  attn_streamk_body<GP, NW, D>(p, blockIdx.x, gridDim.x);
 }
 
 }  // namespace
 
-template <int GP, int KB, int D>
+template <int GP, int D>
 static hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
-  attn_streamk_kernel<GP, kAttnWaves, KB, D><<<dim3(p.num_workgroups), dim3(kAttnWaves * kWave), 0, s>>>(p);
+  attn_streamk_kernel<GP, kAttnWaves, D><<<dim3(p.num_workgroups), dim3(kAttnWaves * kWave), 0, s>>>(p);
   return hipGetLastError();
 }
 
-// Step shape per padded group size: (keys per wave step, pipeline depth).
+// Pipeline depth (32-key steps in flight per wave while one is computed): 1 by
+// default (the registers of a step drain to LDS as it begins), 2..3 selectable.
 template <int GP>
 static hipError_t launch_gp(const AttnParams& p, hipStream_t s) {
   switch (p.step_variant) {
-    case 0:  // default for the group size
-      if constexpr (GP >= 8) return launch_variant<GP, 16, 3>(p, s); else return launch_variant<GP, 32, 2>(p, s);
-    case 1: return launch_variant<GP, 32, 2>(p, s);
-    case 2: return launch_variant<GP, 16, 2>(p, s);
-    case 3: return launch_variant<GP, 16, 3>(p, s);
-    case 4: return launch_variant<GP, 16, 4>(p, s);
+    case 0: return launch_variant<GP, 1>(p, s);
+    case 1: return launch_variant<GP, 1>(p, s);
+    case 2: return launch_variant<GP, 2>(p, s);
+    case 3: return launch_variant<GP, 3>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

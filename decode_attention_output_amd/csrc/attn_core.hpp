@@ -6,17 +6,26 @@
 // Matmul 独立 TileShape 配置 F-16", section 代码对比): scores = q_grouped x
 // k_cache^T in fp32, scaled softmax, attn_weights x v_cache.
 //
-// Per wavefront and per 32-key block:
-//   QK^T  MFMA 16x16x32 bf16. A = the G query rows of the group (rows G..15
-//         are zero: a tiny M never grows past one operand); B = K^T, loaded
-//         straight from HBM in the operand layout, 16 bytes per lane.
-//   softmax online in log2 units (scores times scale*log2 e), block max over
-//         DPP rows, lazy rescale: the reference max moves only when a block
-//         beats it by more than 8, so weights stay <= 2^8.
-//   PV    fp32 on the vector ALUs (weights are not rounded to bf16); a lane
-//         owns 8 dims of 8 keys, V loaded as whole 256-byte rows.
-// Loads of block i+1 are issued before block i is computed (two register
-// sets), so every wave keeps 16 KiB of K/V requests in flight.
+// Per wavefront and per 32-key step:
+//   loads  K and V rows straight from HBM, 1 KiB per load instruction (four
+//          whole 256-byte rows), the access pattern that streams fastest;
+//          the tile is parked in the wave's own LDS stage (rows padded by 16
+//          bytes, so that the operand reads below are free of bank conflicts)
+//          and the registers take the loads of a later step at once.
+//   S^T    = K x Q^T on MFMA 16x16x32 bf16: A = 16 keys read back from LDS in
+//          the operand layout, B = the query group (columns G..15 zero). A lane
+//          ends up with the 8 scores of one query for keys {4g..4g+3,
+//          16+4g..16+4g+3} (g = lane / 16), which is exactly its share of the
+//          A operand of the next product, so the weights never leave registers.
+//   softmax online in log2 units (scores times scale*log2 e); the block max
+//          meets across the four lane groups; lazy rescale: the reference max
+//          moves only when a block beats it by more than 8, so weights <= 2^8.
+//   PV     O = P x V on MFMA 16x16x32 bf16 with fp32 accumulation. P is split
+//          into three bf16 terms (hi and mid by truncation, lo rounded), whose
+//          sum is P within 2^-23 relative, about fp32's own rounding, so the
+//          weights are not coarsened to bf16. V reaches the B layout through
+//          the LDS transpose read: in each 16-lane group, lane i's element r
+//          is element i%4 of the 8 bytes addressed by lane 4r + i/4.
 #pragma once
 
 #include "gfx950.hpp"
@@ -61,31 +70,28 @@ __device__ __forceinline__ void rsrc_st8_coherent(rsrc_t r, uint32_t off, uint2 
 }
 
 // ---- per-wave running state ----
-template <int GP>
+// The wave's 16 MFMA columns are query rows (G valid, the rest zero queries).
 struct AttnWave {
-  float m_ref[4];  // row group grp: query grp*4 + r
-  float l_acc[4];  // per-lane partial sum of weights (key column of this lane)
-  float acc[GP][8];  // un-normalised output, dims col*8..+8, keys of row group grp
+  float m_ref;   // reference max of query lane%16 (log2 units), equal in the 4 lane groups
+  float l_acc;   // sum of this lane's weights of query lane%16
+  f32x4_t o[8];  // O[query 4g + r][dim 16j + lane%16] in element r of o[j]
 
   __device__ __forceinline__ void reset() {
+    m_ref = -INFINITY;
+    l_acc = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m_ref[r] = -INFINITY;
-      l_acc[r] = 0.f;
-    }
-#pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+    for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 };
 
-// Keys one wave handles per step: KB = 32 (two 16-key MFMA tiles) or 16 (one
-// tile, for large groups whose accumulators leave fewer registers free).
-template <int KB>
+constexpr int kStepKeys = 32;                     // keys per wave step
+constexpr int kStageRow = kRowBytes + 16;         // padded LDS row: consecutive rows 4 banks apart
+constexpr int kStageTile = kStepKeys * kStageRow; // one 32-key K or V tile
+constexpr int kStageBytes = 2 * kStageTile;       // LDS of one wave: K tile, V tile
+
+// One step's K and V as loaded: element c holds row 4c + lane/16, bytes (lane%16)*16.
 struct KVTile {
-  uint4 k[KB / 16][4];  // 16-key tiles, MFMA B layout
-  uint4 v[KB / 4];      // keys grp + 4i, dims col*8..+8
+  uint4 k[8], v[8];
 };
 
 // Everything a wave needs to know about the (batch, kv head) it works on.
@@ -95,191 +101,199 @@ struct AttnSeg {
   int G;          // query heads of the group
   float scale_log2;
   float scale;
-  float* dbg;     // scaled scores of query row 0 of the group, or null; row stride dbg_stride
+  float* dbg;     // scaled scores of the group's first query head, or null; row stride dbg_stride
   int dbg_stride;
 };
 
+// B operand of S^T = K x Q^T: lane (query col, group grp) holds dims
+// kk*32 + grp*8 .. +8 of its query (zero for col >= G).
 __device__ __forceinline__ void load_query(uint4 (&qa)[4], const uint16_t* q_rows, int G, int col, int grp) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
     qa[kk] = (col < G) ? ld16(q_rows + (size_t)col * kHeadDim + kk * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
 }
 
-template <int KB>
-__device__ __forceinline__ void load_kv(KVTile<KB>& t, const AttnSeg& sg, int key0, int col, int grp) {
+__device__ __forceinline__ void load_kv(KVTile& t, const AttnSeg& sg, int key0, int lane) {
+  const uint32_t off = (uint32_t)(key0 + (lane >> 4)) * kRowBytes + (lane & 15) * 16;
 #pragma unroll
-  for (int tt = 0; tt < KB / 16; ++tt) {
-    const uint32_t row = (uint32_t)(key0 + 16 * tt + col) * kRowBytes;
+  for (int c = 0; c < 8; ++c) t.k[c] = rsrc_ld16(sg.K, off + c * 4 * kRowBytes);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) t.k[tt][kk] = rsrc_ld16(sg.K, row + kk * 64 + grp * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < KB / 4; ++i) t.v[i] = rsrc_ld16(sg.V, (uint32_t)(key0 + grp + 4 * i) * kRowBytes + col * 16);
+  for (int c = 0; c < 8; ++c) t.v[c] = rsrc_ld16(sg.V, off + c * 4 * kRowBytes);
 }
 
-// One KB-key step starting at key0; keys >= end are masked out.
-template <int GP, int KB>
-__device__ __forceinline__ void attn_block(AttnWave<GP>& w, const KVTile<KB>& t, const uint4 (&qa)[4],
-                                           const AttnSeg& sg, int key0, int end, float* sp, int col, int grp) {
-  constexpr int NTL = KB / 16;
-  f32x4_t sc[NTL];
+__device__ __forceinline__ void stage_kv(char* stage, const KVTile& t, int lane) {
+  char* p = stage + (lane >> 4) * kStageRow + (lane & 15) * 16;
 #pragma unroll
-  for (int tt = 0; tt < NTL; ++tt) {
+  for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(p + c * 4 * kStageRow) = t.k[c];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(p + kStageTile + c * 4 * kStageRow) = t.v[c];
+}
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+
+// LDS transpose read of four 16-bit elements (see the header comment).
+__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
+  const bf16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4_t*)(__attribute__((address_space(3))) char*)(const_cast<char*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// bf16 pair of two floats whose low 16 bits are zero: the high halves.
+__device__ __forceinline__ uint32_t pack_hi(float a, float b) {
+  return (__builtin_bit_cast(uint32_t, a) >> 16) | (__builtin_bit_cast(uint32_t, b) & 0xffff0000u);
+}
+// Round a finite float to bf16 (nearest, ties to even), as a 32-bit pattern.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
+}
+
+// One 32-key step starting at key0, whose K/V tile is in the wave's stage;
+// keys >= end are masked out.
+template <int GP>
+__device__ __forceinline__ void attn_step(AttnWave& w, const char* stage, const uint4 (&qb)[4], const AttnSeg& sg,
+                                          int key0, int end, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  // ---- S^T = K x Q^T, two 16-key tiles ----
+  f32x4_t sc[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
     sc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const char* kr = stage + (16 * tt + i) * kStageRow + g * 16;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) sc[tt] = mfma_bf16(qa[kk], t.k[tt][kk], sc[tt]);
+    for (int kk = 0; kk < 4; ++kk) sc[tt] = mfma_bf16(*reinterpret_cast<const uint4*>(kr + kk * 64), qb[kk], sc[tt]);
   }
-  float s2[NTL][4];
+  // lane (i, g) holds the scores of query i for keys 16tt + 4g + r
+  float s2[2][4];
 #pragma unroll
-  for (int tt = 0; tt < NTL; ++tt) {
-    const int key = key0 + 16 * tt + col;
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s2[tt][r] = (key < end) ? sc[tt][r] * sg.scale_log2 : -INFINITY;
-  }
-  if (sg.dbg) {
+    for (int r = 0; r < 4; ++r) s2[tt][r] = (key0 + 16 * tt + 4 * g + r < end) ? sc[tt][r] * sg.scale_log2 : -INFINITY;
+  if (sg.dbg && i < sg.G) {
 #pragma unroll
-    for (int tt = 0; tt < NTL; ++tt) {
-      const int key = key0 + 16 * tt + col;
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = grp * 4 + r;
-        if (row < sg.G && key < end) sg.dbg[(size_t)row * sg.dbg_stride + key] = sc[tt][r] * sg.scale;
+        const int key = key0 + 16 * tt + 4 * g + r;
+        if (key < end) sg.dbg[(size_t)i * sg.dbg_stride + key] = sc[tt][r] * sg.scale;
       }
-    }
   }
 
-  float bm[4];
-  bool need = false;
+  // ---- online softmax with lazy rescale ----
+  float mx = s2[0][0];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float mx = s2[0][r];
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-    for (int tt = 1; tt < NTL; ++tt) mx = fmaxf(mx, s2[tt][r]);
-    bm[r] = row16_max(mx);
-    need |= bm[r] > w.m_ref[r] + kRescaleSlack;
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s2[tt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (__builtin_amdgcn_ballot_w64(mx > w.m_ref + kRescaleSlack) != 0) {
+    const float mn = fmaxf(w.m_ref, mx);
+    const float alpha = w.m_ref == -INFINITY ? 0.f : exp2f(w.m_ref - mn);
+    w.m_ref = mn;
+    w.l_acc *= alpha;
+    // accumulator row 4g + r belongs to query 4g + r, whose factor lane 4g + r holds
+    float ar[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w.o[j][r] *= ar[r];
   }
-  if (__builtin_amdgcn_ballot_w64(need) != 0) {
-    float alpha[4];
+  float p[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float mn = fmaxf(w.m_ref[r], bm[r]);
-      alpha[r] = exp2f(w.m_ref[r] - mn);
-      w.m_ref[r] = mn;
-      w.l_acc[r] *= alpha[r];
-    }
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      const float a = readlane_f32(alpha[g & 3], (g >> 2) * 16);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w.acc[g][e] *= a;
-    }
-  }
-  float pw[NTL][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int tt = 0; tt < NTL; ++tt) {
       // a masked key has weight 0 (also while the reference max is still -inf)
-      pw[tt][r] = s2[tt][r] > -INFINITY ? exp2f(s2[tt][r] - w.m_ref[r]) : 0.f;
-      w.l_acc[r] += pw[tt][r];
+      p[tt][r] = s2[tt][r] > -INFINITY ? exp2f(s2[tt][r] - w.m_ref) : 0.f;
+      w.l_acc += p[tt][r];
     }
-  }
 
-  // weights to LDS as [key][query] so that each PV lane reads its keys' rows
-  if (grp * 4 < GP) {
+  // ---- A operand of P x V: k index 8g + e is key 4g + e (e < 4), 16 + 4g + e - 4 ----
+  // three bf16 terms per weight: hi and mid by truncation, lo rounded
+  float hi[2][4], mid[2][4], lo[2][4];
 #pragma unroll
-    for (int tt = 0; tt < NTL; ++tt) {
-      const int key = 16 * tt + col;
-      if constexpr (GP >= 4) {
-        *reinterpret_cast<float4*>(sp + key * GP + grp * 4) = make_float4(pw[tt][0], pw[tt][1], pw[tt][2], pw[tt][3]);
-      } else {
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int r = 0; r < GP; ++r) sp[key * GP + r] = pw[tt][r];
-      }
+    for (int r = 0; r < 4; ++r) {
+      hi[tt][r] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p[tt][r]) & 0xffff0000u);
+      const float r1 = p[tt][r] - hi[tt][r];
+      mid[tt][r] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, r1) & 0xffff0000u);
+      lo[tt][r] = __builtin_bit_cast(float, bf16_bits_rne(r1 - mid[tt][r]));
     }
-  }
-  wave_lds_fence();
+  auto pack = [](const float (&x)[2][4]) {
+    return make_uint4(pack_hi(x[0][0], x[0][1]), pack_hi(x[0][2], x[0][3]), pack_hi(x[1][0], x[1][1]),
+                      pack_hi(x[1][2], x[1][3]));
+  };
+  const uint4 a_hi = pack(hi), a_mid = pack(mid), a_lo = pack(lo);
 
+  // ---- O += P x V, 16 dims per product ----
+  const char* vt = stage + kStageTile + (4 * g + (i >> 2)) * kStageRow + (i & 3) * 8;
+  uint4 vb[8];
 #pragma unroll
-  for (int i = 0; i < KB / 4; ++i) {
-    const int key = grp + 4 * i;
-    float vv[8];
-    unpack_bf16x8(t.v[i], vv);
-    float pg[GP];
-    if constexpr (GP >= 4) {
-#pragma unroll
-      for (int g4 = 0; g4 < GP / 4; ++g4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(sp + key * GP + g4 * 4);
-        pg[g4 * 4 + 0] = t4.x;
-        pg[g4 * 4 + 1] = t4.y;
-        pg[g4 * 4 + 2] = t4.z;
-        pg[g4 * 4 + 3] = t4.w;
-      }
-    } else {
-#pragma unroll
-      for (int g = 0; g < GP; ++g) pg[g] = sp[key * GP + g];
-    }
-#pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w.acc[g][e] = fmaf(pg[g], vv[e], w.acc[g][e]);
+  for (int j = 0; j < 8; ++j) {
+    const uint2 v0 = lds_read_tr16(vt + j * 32);
+    const uint2 v1 = lds_read_tr16(vt + 16 * kStageRow + j * 32);
+    vb[j] = make_uint4(v0.x, v0.y, v1.x, v1.y);
   }
-  wave_lds_fence();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w.o[j] = mfma_bf16(a_hi, vb[j], w.o[j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w.o[j] = mfma_bf16(a_mid, vb[j], w.o[j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w.o[j] = mfma_bf16(a_lo, vb[j], w.o[j]);
 }
 
-// The wave's steps first, first+step, ... (n of them, KB keys each). The loads
-// of the next D-1 steps are in flight while a step is computed (D register
-// sets, indexed statically through the unrolled inner loop).
-template <int GP, int KB, int D>
-__device__ __forceinline__ void attn_wave_steps(AttnWave<GP>& w, const uint4 (&qa)[4], const AttnSeg& sg, int first,
-                                                int step, int n, int end, float* sp, int col, int grp) {
+// The wave's steps first, first+step, ... (n of them, 32 keys each). D
+// register sets: a set is parked in LDS as its step begins and at once takes
+// the loads of the step D later, so D steps are in flight during a step.
+template <int GP, int D>
+__device__ __forceinline__ void attn_wave_steps(AttnWave& w, const uint4 (&qb)[4], const AttnSeg& sg, int first,
+                                                int step, int n, int end, char* stage, int lane) {
   if (n <= 0) return;
-  KVTile<KB> t[D];
+  KVTile t[D];
 #pragma unroll
-  for (int j = 0; j < D - 1; ++j)
-    if (j < n) load_kv<KB>(t[j], sg, (first + j * step) * KB, col, grp);
+  for (int j = 0; j < D; ++j)
+    if (j < n) load_kv(t[j], sg, (first + j * step) * kStepKeys, lane);
   for (int i0 = 0; i0 < n; i0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
       if (i < n) {
-        if (i + D - 1 < n) load_kv<KB>(t[(j + D - 1) % D], sg, (first + (i + D - 1) * step) * KB, col, grp);
-        attn_block<GP, KB>(w, t[j], qa, sg, (first + i * step) * KB, end, sp, col, grp);
+        wave_lds_fence();  // the previous step's LDS reads come first
+        stage_kv(stage, t[j], lane);
+        if (i + D < n) load_kv(t[j], sg, (first + (i + D) * step) * kStepKeys, lane);
+        wave_lds_fence();
+        attn_step<GP>(w, stage, qb, sg, (first + i * step) * kStepKeys, end, lane);
       }
     }
   }
+  wave_lds_fence();
 }
 
-// Reduce the wave's state (row sums of l over the 16 key lanes, O over the 4
-// key groups) and park it in LDS: so[g][128], sm[g], sl[g].
+// Park the wave's state in LDS: so[g][128], sm[g], sl[g] for g < GP. These
+// may overlap the wave's own stage (its last reads are complete).
 template <int GP>
-__device__ __forceinline__ void attn_wave_to_lds(AttnWave<GP>& w, float (*so)[kHeadDim], float* sm, float* sl, int col,
-                                                 int grp) {
+__device__ __forceinline__ void attn_wave_to_lds(AttnWave& w, float (*so)[kHeadDim], float* sm, float* sl, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  float l = w.l_acc;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  wave_lds_fence();
 #pragma unroll
-  for (int r = 0; r < 4; ++r) w.l_acc[r] = row16_sum(w.l_acc[r]);
+  for (int r = 0; r < 4; ++r) {
+    const int q = 4 * g + r;
+    if (q < GP) {
 #pragma unroll
-  for (int g = 0; g < GP; ++g)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      w.acc[g][e] += __shfl_xor(w.acc[g][e], 16);
-      w.acc[g][e] += __shfl_xor(w.acc[g][e], 32);
-    }
-  if (grp == 0) {
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      *reinterpret_cast<float4*>(&so[g][col * 8]) = make_float4(w.acc[g][0], w.acc[g][1], w.acc[g][2], w.acc[g][3]);
-      *reinterpret_cast<float4*>(&so[g][col * 8 + 4]) = make_float4(w.acc[g][4], w.acc[g][5], w.acc[g][6], w.acc[g][7]);
+      for (int j = 0; j < 8; ++j) so[q][16 * j + i] = w.o[j][r];
     }
   }
-  if (col == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int g = grp * 4 + r;
-      if (g < GP) {
-        sm[g] = w.m_ref[r];
-        sl[g] = w.l_acc[r];
-      }
-    }
+  if (g == 0 && i < GP) {
+    sm[i] = w.m_ref;
+    sl[i] = l;
   }
 }
 

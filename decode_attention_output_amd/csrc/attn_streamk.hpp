@@ -27,17 +27,24 @@ __device__ __forceinline__ long range_bound(long i, long T, long W) { return T >
 __device__ __forceinline__ long range_owner(long x, long T, long W) { return T >= W ? ((x + 1) * W - 1) / T : x; }
 
 // One workgroup's share of the stream-K attention: workgroup `wg` of `W`.
-template <int GP, int NW, int KB, int D>
+template <int GP, int NW, int D>
 __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, long W) {
   constexpr int NT = NW * kWave;
+  constexpr int kWaveOut = GP * kHeadDim * 4;  // a wave's un-normalised output in its stage
+  static_assert(kWaveOut + 2 * GP * 4 <= kStageBytes, "a wave's output fits its stage");
+  static_assert(NT * 24 <= kStageBytes && NT * 4 <= kStageBytes, "merge scratch fits one stage");
   __shared__ int s_pre[kMaxAttnBatch + 1];  // blocks of the sequences before batch b (per kv head)
   __shared__ int s_len[kMaxAttnBatch];
-  __shared__ int s_scan[NT];
-  __shared__ float s_p[NW][KB * GP];
-  __shared__ float s_o[NW][GP][kHeadDim];
-  __shared__ float s_m[NW][GP], s_l[NW][GP];
-  __shared__ float s_cm[NT], s_cl[NT];
-  __shared__ float4 s_co[NT];
+  // one K/V stage per wave; the same bytes later hold the waves' outputs and
+  // the merge scratch (each use is separated from the next by a barrier)
+  __shared__ __attribute__((aligned(16))) char s_stage[NW * kStageBytes];
+  int* const s_scan = reinterpret_cast<int*>(s_stage);
+  float* const s_cm = reinterpret_cast<float*>(s_stage);
+  float* const s_cl = s_cm + NT;
+  float4* const s_co = reinterpret_cast<float4*>(s_cl + NT);
+  auto s_o = [&](int w) { return reinterpret_cast<float (*)[kHeadDim]>(s_stage + w * kStageBytes); };
+  auto s_m = [&](int w) { return reinterpret_cast<float*>(s_stage + w * kStageBytes + kWaveOut); };
+  auto s_l = [&](int w) { return reinterpret_cast<float*>(s_stage + w * kStageBytes + kWaveOut + GP * 4); };
 
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int col = lane & 15, grp = lane >> 4;
@@ -77,7 +84,11 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   __syncthreads();
 
   DA_TRACE(1);
-  const long T = (long)Hkv * s_pre[B];
+  // Values read from LDS are per-lane to the compiler; those that are the same
+  // in every lane are made wave-uniform, so that the buffer descriptors built
+  // from them live in scalar registers (a per-lane descriptor would make every
+  // load a loop over the distinct values).
+  const long T = (long)Hkv * uniform(s_pre[B]);
   long x = range_bound(wg, T, W);
   const long xe = range_bound(wg + 1, T, W);
   const rsrc_t part_o = make_rsrc(p.part_o, p.part_o_bytes);
@@ -94,18 +105,19 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
     int lo = 0, hi = B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if ((long)Hkv * s_pre[mid] <= x) lo = mid; else hi = mid;
+      if ((long)Hkv * uniform(s_pre[mid]) <= x) lo = mid; else hi = mid;
     }
     const int b = lo;
-    const int nb = s_pre[b + 1] - s_pre[b];
-    const long seg0 = (long)Hkv * s_pre[b];
+    const int pre_b = uniform(s_pre[b]);
+    const int nb = uniform(s_pre[b + 1]) - pre_b;
+    const long seg0 = (long)Hkv * pre_b;
     const int h = (int)((x - seg0) / nb);
     const long ss = seg0 + (long)h * nb, se = ss + nb;
     const long pe = min(xe, se);
     const int lb0 = (int)(x - ss), lb1 = (int)(pe - ss);
     const bool whole = (x == ss && pe == se);
     const int seg = b * Hkv + h;
-    const int L = s_len[b];
+    const int L = uniform(s_len[b]);
 
     AttnSeg sg;
     const size_t kv_off = (size_t)seg * p.Lmax * kHeadDim;
@@ -120,15 +132,14 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
 
     uint4 qa[4];
     load_query(qa, p.q + ((size_t)b * p.Hq + (size_t)h * G) * kHeadDim, G, col, grp);
-    AttnWave<GP> aw;
+    AttnWave aw;
     aw.reset();
-    // the piece's keys [lb0*32, min(lb1*32, L)) in steps of KB keys, interleaved over the
+    // the piece's keys [lb0*32, min(lb1*32, L)) in 32-key steps, interleaved over the
     // waves; every step holds at least one key of the sequence
-    constexpr int SPB = kBlockKeys / KB;  // steps per block
-    const int nstep = (min(lb1 * kBlockKeys, L) - lb0 * kBlockKeys + KB - 1) / KB;
+    const int nstep = (min(lb1 * kBlockKeys, L) - lb0 * kBlockKeys + kStepKeys - 1) / kStepKeys;
     const int n = nstep > wave ? (nstep - wave + NW - 1) / NW : 0;
-    attn_wave_steps<GP, KB, D>(aw, qa, sg, lb0 * SPB + wave, NW, n, L, s_p[wave], col, grp);
-    attn_wave_to_lds<GP>(aw, s_o[wave], s_m[wave], s_l[wave], col, grp);
+    attn_wave_steps<GP, D>(aw, qa, sg, lb0 + wave, NW, n, L, s_stage + wave * kStageBytes, lane);
+    attn_wave_to_lds<GP>(aw, s_o(wave), s_m(wave), s_l(wave), lane);
     __syncthreads();
     DA_TRACE(2);
 
@@ -136,15 +147,15 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
     const int slot = seg + (int)wg;
     for (int idx = t; idx < G * 32; idx += NT) {
       const int g = idx >> 5, d4 = idx & 31;
-      float M = s_m[0][g];
+      float M = s_m(0)[g];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m(w)[g]);
       float Ls = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float f = exp2f(s_m[w][g] - M);
-        Ls = fmaf(f, s_l[w][g], Ls);
-        const float4 o4 = *reinterpret_cast<const float4*>(&s_o[w][g][d4 * 4]);
+        const float f = exp2f(s_m(w)[g] - M);
+        Ls = fmaf(f, s_l(w)[g], Ls);
+        const float4 o4 = *reinterpret_cast<const float4*>(&s_o(w)[g][d4 * 4]);
         O[0] = fmaf(f, o4.x, O[0]);
         O[1] = fmaf(f, o4.y, O[1]);
         O[2] = fmaf(f, o4.z, O[2]);
@@ -165,6 +176,8 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
     }
 
     if (!whole) {
+      // (the barrier inside arrive_last_coherent also ends the reads of the waves' outputs,
+      // whose bytes the merge scratch reuses)
       const long first = range_owner(ss, T, W), last = range_owner(se - 1, T, W);
       const int P = (int)(last - first + 1);
       const bool last_piece = arrive_last_coherent(&p.counters[seg], (uint32_t)P);

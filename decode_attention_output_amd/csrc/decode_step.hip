@@ -42,11 +42,16 @@ constexpr int kWeightStages = 8;           // the weight tile is requested in th
 constexpr uint32_t kNoLoad = 0x80000000u;  // buffer offset past every range: the load returns 0, no request
 
 // ---- attention: piece `a` = (sequence a / pieces, piece a % pieces) ----
-template <int GP, int KB, int D>
-__device__ __forceinline__ void piece_attention(const StepParams& p, int a) {
-  __shared__ float s_p[kWaves][KB * GP];
-  __shared__ float s_o[kWaves][GP][kHeadDim];
-  __shared__ float s_m[kWaves][GP], s_l[kWaves][GP];
+// `smem` holds one K/V stage per wave; a wave's output later reuses its stage.
+constexpr int kAttnLds = kWaves * kStageBytes;
+
+template <int GP, int D>
+__device__ __forceinline__ void piece_attention(const StepParams& p, int a, char* smem) {
+  constexpr int kWaveOut = GP * kHeadDim * 4;
+  static_assert(kWaveOut + 2 * GP * 4 <= kStageBytes, "a wave's output fits its stage");
+  auto s_o = [&](int w) { return reinterpret_cast<float (*)[kHeadDim]>(smem + w * kStageBytes); };
+  auto s_m = [&](int w) { return reinterpret_cast<float*>(smem + w * kStageBytes + kWaveOut); };
+  auto s_l = [&](int w) { return reinterpret_cast<float*>(smem + w * kStageBytes + kWaveOut + GP * 4); };
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int col = lane & 15, grp = lane >> 4;
   const int seq = a / p.pieces, piece = a % p.pieces;
@@ -70,13 +75,13 @@ __device__ __forceinline__ void piece_attention(const StepParams& p, int a) {
   sg.scale = 0.f;
   sg.dbg = nullptr;
   sg.dbg_stride = 0;
-  AttnWave<GP> aw;
+  AttnWave aw;
   aw.reset();
-  // the piece's KB-key steps, interleaved over the waves
-  const int nstep = k1 > k0 ? (k1 - k0 + KB - 1) / KB : 0;
+  // the piece's 32-key steps, interleaved over the waves
+  const int nstep = k1 > k0 ? (k1 - k0 + kStepKeys - 1) / kStepKeys : 0;
   const int n = nstep > wave ? (nstep - wave + kWaves - 1) / kWaves : 0;
-  attn_wave_steps<GP, KB, D>(aw, qa, sg, k0 / KB + wave, kWaves, n, L, s_p[wave], col, grp);
-  attn_wave_to_lds<GP>(aw, s_o[wave], s_m[wave], s_l[wave], col, grp);
+  attn_wave_steps<GP, D>(aw, qa, sg, k0 / kStepKeys + wave, kWaves, n, L, smem + wave * kStageBytes, lane);
+  attn_wave_to_lds<GP>(aw, s_o(wave), s_m(wave), s_l(wave), lane);
   __syncthreads();
   DA_TRACE(2);
 
@@ -85,15 +90,15 @@ __device__ __forceinline__ void piece_attention(const StepParams& p, int a) {
   const rsrc_t pml = make_rsrc(p.part_ml, p.part_ml_bytes);
   for (int idx = t; idx < p.G * 32; idx += kThreads) {
     const int g = idx >> 5, d4 = idx & 31;
-    float M = s_m[0][g];
+    float M = s_m(0)[g];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m(w)[g]);
     float Ls = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = s_m[w][g] == -INFINITY ? 0.f : exp2f(s_m[w][g] - M);
-      Ls = fmaf(f, s_l[w][g], Ls);
-      const float4 o4 = *reinterpret_cast<const float4*>(&s_o[w][g][d4 * 4]);
+      const float f = s_m(w)[g] == -INFINITY ? 0.f : exp2f(s_m(w)[g] - M);
+      Ls = fmaf(f, s_l(w)[g], Ls);
+      const float4 o4 = *reinterpret_cast<const float4*>(&s_o(w)[g][d4 * 4]);
       O[0] = fmaf(f, o4.x, O[0]);
       O[1] = fmaf(f, o4.y, O[1]);
       O[2] = fmaf(f, o4.z, O[2]);
@@ -116,16 +121,19 @@ __device__ __forceinline__ void piece_attention(const StepParams& p, int a) {
 
 // ---- projection: column tile r % tiles of K-chunk r / tiles ----
 template <int MB, int TC>
-__device__ __forceinline__ void projection(const StepParams& p, int r) {
+__device__ __forceinline__ void projection(const StepParams& p, int r, char* smem) {
   constexpr int LPR = TC / 8;             // lanes per weight row (16 bytes each)
   constexpr int RPP = kThreads / LPR;     // rows per pass of the workgroup
   constexpr int UR = kRowsPerLane;
   constexpr int KC = UR * RPP;            // rows of the K-chunk
   constexpr int NH = KC / kHeadDim;       // query heads of the chunk
   static_assert(NH >= 1 && UR % kWeightStages == 0, "chunk of whole query heads, staged loads");
-  __shared__ float s_x[KC * MB];          // [row of the chunk][MB] attention output, fp32 of bf16
-  __shared__ float s_cm[kThreads], s_cl[kThreads];
-  __shared__ float4 s_co[kThreads];
+  constexpr int kFinOff = (KC * MB + 6 * kThreads) * 4;
+  static_assert(kFinOff + gemv_finish_lds<MB, TC>() <= kAttnLds, "projection scratch fits the kernel's LDS");
+  float* const s_x = reinterpret_cast<float*>(smem);  // [row of the chunk][MB] attention output, fp32 of bf16
+  float* const s_cm = s_x + KC * MB;
+  float* const s_cl = s_cm + kThreads;
+  float4* const s_co = reinterpret_cast<float4*>(s_cl + kThreads);
   const int t = threadIdx.x;
   const int tile = r % p.tiles, chunk = r / p.tiles;
   const int n = tile * TC + (t % LPR) * 8;
@@ -271,24 +279,23 @@ __device__ __forceinline__ void projection(const StepParams& p, int r) {
   g.kchunk = KC;
   g.ksplit = p.chunks;
   g.tile_n = TC;
-  gemv_finish<MB, TC>(g, acc, tile, chunk, &p.proj_cnt[tile * kCounterStride]);
+  gemv_finish<MB, TC>(g, acc, tile, chunk, &p.proj_cnt[tile * kCounterStride], smem + kFinOff);
   DA_TRACE(12);
 }
 
-template <int GP, int KB, int D, int MB, int TC>
+template <int GP, int D, int MB, int TC>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kAttnLds];
   if ((int)blockIdx.x < p.attn_wgs) {
-    piece_attention<GP, KB, D>(p, (int)blockIdx.x);
+    piece_attention<GP, D>(p, (int)blockIdx.x, smem);
     return;
   }
-  projection<MB, TC>(p, (int)blockIdx.x - p.attn_wgs);
+  projection<MB, TC>(p, (int)blockIdx.x - p.attn_wgs, smem);
 }
 
 template <int GP, int MB, int TC>
 hipError_t launch_step(const StepParams& p, hipStream_t s) {
-  constexpr int KB = GP >= 8 ? 16 : 32;
-  constexpr int D = GP >= 8 ? 3 : 2;
-  decode_step_kernel<GP, KB, D, MB, TC><<<dim3(p.attn_wgs + p.tiles * p.chunks), dim3(kThreads), 0, s>>>(p);
+  decode_step_kernel<GP, 2, MB, TC><<<dim3(p.attn_wgs + p.tiles * p.chunks), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -13,14 +13,21 @@ constexpr int kGemvThreads = 256;
 // (row lanes of a wave by shuffles, the 4 waves in LDS), then write bf16 when
 // the K axis is not split, or store the fp32 partial through device-coherent
 // stores; the last K-chunk of the tile to arrive adds all partials in chunk
-// order (deterministic) and writes bf16. `counter` is the tile's arrival counter.
+// order (deterministic) and writes bf16. `counter` is the tile's arrival counter;
+// `smem` is gemv_finish_lds<MB, TC>() bytes of LDS, 16-byte aligned, that no
+// other thread of the workgroup touches meanwhile.
+template <int MB, int TC>
+constexpr int gemv_finish_lds() {
+  return (kGemvThreads / kWave) * MB * TC * 4 + kGemvThreads * 16;
+}
+
 template <int MB, int TC>
 __device__ __forceinline__ void gemv_finish(const GemvParams& p, float (&acc)[MB][8], int tile, int ks,
-                                            uint32_t* counter) {
+                                            uint32_t* counter, char* smem) {
   constexpr int kStrip = TC;
   constexpr int kLanesPerRow = TC / 8;
-  __shared__ float s_red[kGemvThreads / kWave][MB][kStrip];
-  __shared__ float4 s_fin[kGemvThreads];
+  auto s_red = reinterpret_cast<float (*)[MB][kStrip]>(smem);  // [wave][MB][kStrip]
+  float4* const s_fin = reinterpret_cast<float4*>(smem + (kGemvThreads / kWave) * MB * kStrip * 4);
   const int t = threadIdx.x;
   const int n0 = tile * kStrip;
   // reduce the row lanes of a wave (lanes l, l^LPR, l^2LPR, ...), then the 4 waves

@@ -76,6 +76,9 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// A value that is the same in every lane, moved to a scalar register.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ float readlane_f32(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }

@@ -36,7 +36,7 @@ struct AttnParams {
   float* dbg_lse;           // optional fp32 [B, Hq]
   int B, Hq, Hkv, G, Lmax;
   int num_workgroups;       // stream-K workgroups; slots = num_workgroups + B * Hkv
-  int step_variant;         // 0: default step shape for the group size; 1..4: (32,2) (16,2) (16,3) (16,4)
+  int step_variant;         // 32-key steps in flight per wave: 0 = default (2), else 1..3
   float scale;       // softmax scale (natural units)
   float scale_log2;  // scale * log2(e)
 };

@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
     use_batch(wb, bt + 1);
   }
 
-  gemv_finish<MB, TC>(p, acc, tile, ks, &p.counters[tile]);
+  __shared__ __attribute__((aligned(16))) char s_fin[gemv_finish_lds<MB, TC>()];
+  gemv_finish<MB, TC>(p, acc, tile, ks, &p.counters[tile], s_fin);
 }
 
 // ---- MFMA GEMM: 16 x 64 output tile, K staged 128 rows at a time ----
