@@ -26,18 +26,26 @@ constexpr int kMergeBatch = 16;  // partials whose loads are in flight together 
 __device__ __forceinline__ long range_bound(long i, long T, long W) { return T >= W ? (i * T) / W : (i < T ? i : T); }
 __device__ __forceinline__ long range_owner(long x, long T, long W) { return T >= W ? ((x + 1) * W - 1) / T : x; }
 
-// One workgroup's share of the stream-K attention: workgroup `wg` of `W`.
+// LDS of attn_streamk_body: sequence table, then one K/V stage per wave (the
+// same bytes later hold the waves' outputs and the merge scratch; each use is
+// separated from the next by a barrier).
+constexpr int kAttnTableBytes = ((2 * kMaxAttnBatch + 1) * 4 + 15) / 16 * 16;
+template <int NW>
+constexpr int attn_streamk_lds() {
+  return kAttnTableBytes + NW * kStageBytes;
+}
+
+// One workgroup's share of the stream-K attention: workgroup `wg` of `W`;
+// `smem` is attn_streamk_lds<NW>() bytes of LDS, 16-byte aligned.
 template <int GP, int NW, int D>
-__device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, long W) {
+__device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, long W, char* smem) {
   constexpr int NT = NW * kWave;
   constexpr int kWaveOut = GP * kHeadDim * 4;  // a wave's un-normalised output in its stage
   static_assert(kWaveOut + 2 * GP * 4 <= kStageBytes, "a wave's output fits its stage");
   static_assert(NT * 24 <= kStageBytes && NT * 4 <= kStageBytes, "merge scratch fits one stage");
-  __shared__ int s_pre[kMaxAttnBatch + 1];  // blocks of the sequences before batch b (per kv head)
-  __shared__ int s_len[kMaxAttnBatch];
-  // one K/V stage per wave; the same bytes later hold the waves' outputs and
-  // the merge scratch (each use is separated from the next by a barrier)
-  __shared__ __attribute__((aligned(16))) char s_stage[NW * kStageBytes];
+  int* const s_pre = reinterpret_cast<int*>(smem);  // blocks of the sequences before batch b (per kv head)
+  int* const s_len = s_pre + kMaxAttnBatch + 1;
+  char* const s_stage = smem + kAttnTableBytes;
   int* const s_scan = reinterpret_cast<int*>(s_stage);
   float* const s_cm = reinterpret_cast<float*>(s_stage);
   float* const s_cl = s_cm + NT;

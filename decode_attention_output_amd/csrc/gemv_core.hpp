@@ -123,4 +123,89 @@ __device__ __forceinline__ void gemv_finish(const GemvParams& p, float (&acc)[MB
 }
 
 
+// One GEMV work item: a TC-column tile of the weight (TC*2 bytes of every row)
+// times a K-chunk of rows. Lane t streams 16-byte pieces of rows rr, rr+RPP,
+// ... (rr = t/(TC/8)) of column group t%(TC/8), a batch of kGemvUnroll rows at
+// a time with the next batch in flight while the current one is multiplied.
+// `before_x()` runs (in every thread) after the first weight batch has been
+// requested and before the activation chunk is read; the activations are
+// staged in LDS as fp32 (`s_x`: kchunk * MB floats) and, with COHERENT_X, read
+// with device-coherent loads (they were written earlier in the same launch).
+constexpr int kGemvUnroll = 8;
+
+template <int MB, int TC, bool COHERENT_X, class BeforeX>
+__device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int ks, float* s_x, char* fin_smem,
+                                          BeforeX before_x) {
+  constexpr int kLanesPerRow = TC / 8;
+  constexpr int kRowLanes = kGemvThreads / kLanesPerRow;
+  const int n0 = tile * TC;
+  const int k0 = ks * p.kchunk;
+  const int kn = min(p.kchunk, p.K - k0);
+  const int t = threadIdx.x;
+  const int cg = t % kLanesPerRow, rr = t / kLanesPerRow;
+  const int n = n0 + cg * 8;
+  const bool col_ok = n < p.N;
+  const uint16_t* __restrict__ wbase = p.w + (size_t)k0 * p.N + n;
+  const int nbatch = (kn + kRowLanes * kGemvUnroll - 1) / (kRowLanes * kGemvUnroll);
+
+  auto load_batch = [&](uint4 (&wv)[kGemvUnroll], int bt) {
+#pragma unroll
+    for (int u = 0; u < kGemvUnroll; ++u) {
+      const int kk = bt * kRowLanes * kGemvUnroll + rr + kRowLanes * u;
+      wv[u] = (col_ok && kk < kn) ? ld16(wbase + (size_t)kk * p.N) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  float acc[MB][8];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
+  auto use_batch = [&](const uint4 (&wv)[kGemvUnroll], int bt) {
+#pragma unroll
+    for (int u = 0; u < kGemvUnroll; ++u) {
+      const int kk = bt * kRowLanes * kGemvUnroll + rr + kRowLanes * u;
+      if (kk < kn) {
+        float wf[8];
+        unpack_bf16x8(wv[u], wf);
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          const float xm = s_x[kk * MB + m];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[m][e] = fmaf(xm, wf[e], acc[m][e]);
+        }
+      }
+    }
+  };
+
+  uint4 wa[kGemvUnroll], wb[kGemvUnroll];
+  load_batch(wa, 0);
+  before_x();
+  // activations in groups of 4 (K and the chunk are multiples of 8)
+  const rsrc_t xr = make_rsrc(p.x, (uint32_t)min((size_t)p.M * p.K * 2, (size_t)0x7fffffff));
+  for (int idx = t; idx < MB * (kn / 4); idx += kGemvThreads) {
+    const int m = idx / (kn / 4), k4 = idx % (kn / 4);
+    uint2 v = make_uint2(0, 0);
+    if (m < p.M) {
+      const uint32_t off = (uint32_t)(((size_t)m * p.K + k0 + 4 * k4) * 2);
+      if constexpr (COHERENT_X)
+        v = rsrc_ld8_coherent(xr, off);
+      else
+        v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(xr, (int)off, 0, 0));
+    }
+    s_x[(4 * k4 + 0) * MB + m] = bf16_lo(v.x);
+    s_x[(4 * k4 + 1) * MB + m] = bf16_hi(v.x);
+    s_x[(4 * k4 + 2) * MB + m] = bf16_lo(v.y);
+    s_x[(4 * k4 + 3) * MB + m] = bf16_hi(v.y);
+  }
+  __syncthreads();
+  for (int bt = 0; bt < nbatch; bt += 2) {
+    if (bt + 1 < nbatch) load_batch(wb, bt + 1);
+    use_batch(wa, bt);
+    if (bt + 1 >= nbatch) break;
+    if (bt + 2 < nbatch) load_batch(wa, bt + 2);
+    use_batch(wb, bt + 1);
+  }
+  gemv_finish<MB, TC>(p, acc, tile, ks, &p.counters[tile], fin_smem);
+}
+
 }  // namespace da

@@ -23,79 +23,13 @@ namespace da {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;                 // weight rows per lane per batch (128 B in flight per lane)
 
-// GEMV workgroup: a TC-column tile of the weight (TC*2 bytes of every row)
-// times a K-chunk of rows. Lane t streams 16-byte pieces of rows rr, rr+RPP,
-// ... (rr = t/(TC/8)) of column group t%(TC/8), a batch of kUnroll rows at a
-// time with the next batch in flight while the current one is multiplied.
-// The activation chunk is staged in LDS (as fp32) after the first weight
-// batch has been issued.
+// GEMV workgroup: one work item of gemv_core.hpp per workgroup.
 template <int MB, int TC>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvParams p) {
-  constexpr int kStrip = TC;
-  constexpr int kLanesPerRow = TC / 8;
-  constexpr int kRowLanes = kThreads / kLanesPerRow;
   extern __shared__ float s_x[];  // [kchunk][MB]
-
-  const int tile = blockIdx.x, ks = blockIdx.y;
-  const int n0 = tile * kStrip;
-  const int k0 = ks * p.kchunk;
-  const int kn = min(p.kchunk, p.K - k0);
-  const int t = threadIdx.x;
-  const int cg = t % kLanesPerRow, rr = t / kLanesPerRow;
-  const int n = n0 + cg * 8;
-  const bool col_ok = n < p.N;
-  const uint16_t* __restrict__ wbase = p.w + (size_t)k0 * p.N + n;
-  const int nbatch = (kn + kRowLanes * kUnroll - 1) / (kRowLanes * kUnroll);
-
-  auto load_batch = [&](uint4 (&wv)[kUnroll], int bt) {
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int kk = bt * kRowLanes * kUnroll + rr + kRowLanes * u;
-      wv[u] = (col_ok && kk < kn) ? ld16(wbase + (size_t)kk * p.N) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  float acc[MB][8];
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
-  auto use_batch = [&](const uint4 (&wv)[kUnroll], int bt) {
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int kk = bt * kRowLanes * kUnroll + rr + kRowLanes * u;
-      if (kk < kn) {
-        float wf[8];
-        unpack_bf16x8(wv[u], wf);
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          const float xm = s_x[kk * MB + m];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[m][e] = fmaf(xm, wf[e], acc[m][e]);
-        }
-      }
-    }
-  };
-
-  uint4 wa[kUnroll], wb[kUnroll];
-  load_batch(wa, 0);
-  for (int idx = t; idx < MB * kn; idx += kThreads) {
-    const int m = idx / kn, kk = idx % kn;
-    const uint16_t xw = (m < p.M) ? p.x[(size_t)m * p.K + k0 + kk] : (uint16_t)0;
-    s_x[kk * MB + m] = __builtin_bit_cast(float, (uint32_t)xw << 16);
-  }
-  __syncthreads();
-  for (int bt = 0; bt < nbatch; bt += 2) {
-    if (bt + 1 < nbatch) load_batch(wb, bt + 1);
-    use_batch(wa, bt);
-    if (bt + 1 >= nbatch) break;
-    if (bt + 2 < nbatch) load_batch(wa, bt + 2);
-    use_batch(wb, bt + 1);
-  }
-
   __shared__ __attribute__((aligned(16))) char s_fin[gemv_finish_lds<MB, TC>()];
-  gemv_finish<MB, TC>(p, acc, tile, ks, &p.counters[tile], s_fin);
+  gemv_item<MB, TC, false>(p, blockIdx.x, blockIdx.y, s_x, s_fin, [] {});
 }
 
 // ---- MFMA GEMM: 16 x 64 output tile, K staged 128 rows at a time ----
