@@ -133,7 +133,12 @@ constexpr int kStepResident = 512;        // workgroups resident at once: two 25
 constexpr int kStepAttnTarget = 128;      // attention workgroups aimed at
 constexpr int kStepMaxAttn = 384;         // at most, leaving room for the projection
 constexpr int kPieceGrain = 128;          // keys of a piece: a multiple of 4 waves x 32 keys
-constexpr uint32_t kStepWeightDelay = 0;  // 100 MHz ticks before the projection requests its weight
+// The projection may request its weight kStepWeightDelay ticks (100 MHz)
+// after it starts, to let the attention's first loads go ahead. Measured on
+// the 32/8-head, 2048-key, 4096-hidden step: 1.5 us of delay gains ~1.3 us
+// per step when the inputs are cache-resident but loses ~0.3 us when they
+// come from HBM, so it is off.
+constexpr uint32_t kStepWeightDelay = 0;
 constexpr uint32_t kStepStageGap = 0;     // ticks between the 8 stages of those requests
 
 struct StepPlan {

@@ -274,6 +274,31 @@ __device__ __forceinline__ void attn_wave_steps(AttnWave& w, const uint4 (&qb)[4
   wave_lds_fence();
 }
 
+// The same with one register set, the first tile already loaded (through
+// resources that may reach past `end`): rows of it at or past `end` are
+// zeroed before use, so that whatever the cache holds there (NaN padding
+// included) never meets a weight.
+template <int GP>
+__device__ __forceinline__ void attn_wave_steps_preloaded(AttnWave& w, KVTile& t, const uint4 (&qb)[4],
+                                                          const AttnSeg& sg, int first, int step, int n, int end,
+                                                          char* stage, int lane) {
+  if (n <= 0) return;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    if (first * kStepKeys + 4 * c + (lane >> 4) >= end) {
+      t.k[c] = make_uint4(0, 0, 0, 0);
+      t.v[c] = make_uint4(0, 0, 0, 0);
+    }
+  for (int i = 0; i < n; ++i) {
+    wave_lds_fence();  // the previous step's LDS reads come first
+    stage_kv(stage, t, lane);
+    if (i + 1 < n) load_kv(t, sg, (first + (i + 1) * step) * kStepKeys, lane);
+    wave_lds_fence();
+    attn_step<GP>(w, stage, qb, sg, (first + i * step) * kStepKeys, end, lane);
+  }
+  wave_lds_fence();
+}
+
 // Park the wave's state in LDS: so[g][128], sm[g], sl[g] for g < GP. These
 // may overlap the wave's own stage (its last reads are complete).
 template <int GP>

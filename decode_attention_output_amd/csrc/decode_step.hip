@@ -45,7 +45,7 @@ constexpr uint32_t kNoLoad = 0x80000000u;  // buffer offset past every range: th
 // `smem` holds one K/V stage per wave; a wave's output later reuses its stage.
 constexpr int kAttnLds = kWaves * kStageBytes;
 
-template <int GP, int D>
+template <int GP>
 __device__ __forceinline__ void piece_attention(const StepParams& p, int a, char* smem) {
   constexpr int kWaveOut = GP * kHeadDim * 4;
   static_assert(kWaveOut + 2 * GP * 4 <= kStageBytes, "a wave's output fits its stage");
@@ -58,15 +58,26 @@ __device__ __forceinline__ void piece_attention(const StepParams& p, int a, char
   const int b = seq / p.Hkv, h = seq % p.Hkv;
   DA_TRACE(0);
 
+  // the wave's first 32-key step is requested before the sequence length is
+  // known, through resources bounded by the cache's rows (always inside the
+  // allocation); rows past the length are zeroed once it is known
+  const size_t kv_off = (size_t)seq * p.Lmax * kHeadDim;
+  const int k0 = piece * p.piece_keys;
+  const int first = k0 / kStepKeys + wave;
+  KVTile t0;
+  if (first * kStepKeys < min(k0 + p.piece_keys, p.Lmax)) {
+    AttnSeg cap;
+    cap.K = make_rsrc(p.k + kv_off, (uint32_t)p.Lmax * kRowBytes);
+    cap.V = make_rsrc(p.v + kv_off, (uint32_t)p.Lmax * kRowBytes);
+    load_kv(t0, cap, first * kStepKeys, lane);
+  }
   uint4 qa[4];
   load_query(qa, p.q + ((size_t)b * p.Hq + (size_t)h * p.G) * kHeadDim, p.G, col, grp);
   const int L = min(max(p.seq_lens[b], 0), p.Lmax);
-  const int k0 = piece * p.piece_keys;
   const int k1 = min(k0 + p.piece_keys, L);
   DA_TRACE(1);
 
   AttnSeg sg;
-  const size_t kv_off = (size_t)seq * p.Lmax * kHeadDim;
   sg.K = make_rsrc(p.k + kv_off, (uint32_t)L * kRowBytes);
   sg.V = make_rsrc(p.v + kv_off, (uint32_t)L * kRowBytes);
   sg.L = L;
@@ -80,7 +91,7 @@ __device__ __forceinline__ void piece_attention(const StepParams& p, int a, char
   // the piece's 32-key steps, interleaved over the waves
   const int nstep = k1 > k0 ? (k1 - k0 + kStepKeys - 1) / kStepKeys : 0;
   const int n = nstep > wave ? (nstep - wave + kWaves - 1) / kWaves : 0;
-  attn_wave_steps<GP, D>(aw, qa, sg, k0 / kStepKeys + wave, kWaves, n, L, smem + wave * kStageBytes, lane);
+  attn_wave_steps_preloaded<GP>(aw, t0, qa, sg, first, kWaves, n, L, smem + wave * kStageBytes, lane);
   attn_wave_to_lds<GP>(aw, s_o(wave), s_m(wave), s_l(wave), lane);
   __syncthreads();
   DA_TRACE(2);
@@ -283,11 +294,11 @@ __device__ __forceinline__ void projection(const StepParams& p, int r, char* sme
   DA_TRACE(12);
 }
 
-template <int GP, int D, int MB, int TC>
+template <int GP, int MB, int TC>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kAttnLds];
   if ((int)blockIdx.x < p.attn_wgs) {
-    piece_attention<GP, D>(p, (int)blockIdx.x, smem);
+    piece_attention<GP>(p, (int)blockIdx.x, smem);
     return;
   }
   projection<MB, TC>(p, (int)blockIdx.x - p.attn_wgs, smem);
@@ -295,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams p) 
 
 template <int GP, int MB, int TC>
 hipError_t launch_step(const StepParams& p, hipStream_t s) {
-  decode_step_kernel<GP, 2, MB, TC><<<dim3(p.attn_wgs + p.tiles * p.chunks), dim3(kThreads), 0, s>>>(p);
+  decode_step_kernel<GP, MB, TC><<<dim3(p.attn_wgs + p.tiles * p.chunks), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 
