@@ -21,7 +21,7 @@ namespace {
 
 using da::kHeadDim;
 
-constexpr int kAttnWorkgroups = 512;        // stream-K attention: two per compute unit
+constexpr int kAttnWorkgroups = 256;        // stream-K attention: one per compute unit (longer ranges, fewer merges)
 constexpr int kAttnBlockKeys = 32;          // keys per wave step
 constexpr int kTargetProjWorkgroups = 512;   // GEMV: two per compute unit
 constexpr int kTargetGemmWorkgroups = 512;   // MFMA GEMM: two per compute unit
