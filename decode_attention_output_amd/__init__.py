@@ -42,6 +42,22 @@ EXPORTED = (
 )
 
 
+class DecodeAttnTiles(ctypes.Structure):
+    """Tile override of one call (decode_attn_tiles_t); zero fields keep the built-in choice."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit",
+                                              "step_mode")]
+
+
+def make_tiles(tiles) -> Optional[DecodeAttnTiles]:
+    """None, a DecodeAttnTiles or a dict of its fields -> DecodeAttnTiles or None."""
+    if tiles is None or isinstance(tiles, DecodeAttnTiles):
+        return tiles
+    unknown = set(tiles) - {n for n, _ in DecodeAttnTiles._fields_}
+    if unknown:
+        raise ValueError("unknown tile fields: %s" % sorted(unknown))
+    return DecodeAttnTiles(**{k: int(v) for k, v in tiles.items()})
+
+
 class DecodeAttnShape(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32),
@@ -56,6 +72,7 @@ class DecodeAttnShape(ctypes.Structure):
         ("flags", ctypes.c_uint32),
         ("debug_scores", ctypes.c_void_p),
         ("debug_lse", ctypes.c_void_p),
+        ("tiles", ctypes.POINTER(DecodeAttnTiles)),
     ]
 
 
@@ -128,10 +145,17 @@ decode_attn_status_str = status_str
 
 
 def make_shape(batch, num_q_heads, num_kv_heads, max_seq_len, hidden=0, head_dim=DA_HEAD_DIM, softmax_scale=0.0,
-               workspace=None, workspace_bytes=0, flags=0, debug_scores=None, debug_lse=None) -> DecodeAttnShape:
-    return DecodeAttnShape(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(max_seq_len),
-                           int(hidden), float(softmax_scale), workspace, int(workspace_bytes), int(flags),
-                           debug_scores, debug_lse)
+               workspace=None, workspace_bytes=0, flags=0, debug_scores=None, debug_lse=None,
+               tiles=None) -> DecodeAttnShape:
+    """The C shape struct; ``tiles`` (a dict or DecodeAttnTiles) is kept alive by the struct."""
+    shape = DecodeAttnShape(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(max_seq_len),
+                            int(hidden), float(softmax_scale), workspace, int(workspace_bytes), int(flags),
+                            debug_scores, debug_lse)
+    t = make_tiles(tiles)
+    if t is not None:
+        shape._tiles = t
+        shape.tiles = ctypes.pointer(t)
+    return shape
 
 
 def decode_attn_workspace_size(shape: DecodeAttnShape) -> int:
@@ -197,9 +221,11 @@ class Workspace:
 
 
 def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Optional[Workspace] = None,
-                    softmax_scale: float = 0.0, debug_scores=None, debug_lse=None, stream=None, separate=False):
+                    softmax_scale: float = 0.0, debug_scores=None, debug_lse=None, stream=None, separate=False,
+                    tiles=None):
     """One decode step: returns out [B, hidden] bf16. ``separate`` asks for two
-    launches (attention, projection) where the plan would use one."""
+    launches (attention, projection) where the plan would use one; ``tiles``
+    overrides the tile choice (decode_attn_tiles_t fields)."""
     torch = _check_dev("q", q, _torch().bfloat16)
     _check_dev("k_cache", k_cache, torch.bfloat16)
     _check_dev("v_cache", v_cache, torch.bfloat16)
@@ -212,7 +238,7 @@ def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace
         out = torch.empty((B, hidden), dtype=torch.bfloat16, device=q.device)
     flags = (DA_FLAG_DEBUG_SCORES if debug_scores is not None else 0) | (DA_FLAG_SEPARATE if separate else 0)
     shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale, flags=flags, debug_scores=_ptr(debug_scores),
-                       debug_lse=_ptr(debug_lse))
+                       debug_lse=_ptr(debug_lse), tiles=tiles)
     need = decode_attn_workspace_size(shape)
     ws = (workspace or Workspace(q.device)).get(need)
     shape.workspace = _ptr(ws)
@@ -226,7 +252,7 @@ def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace
 
 
 def decode_attn_only(q, k_cache, v_cache, seq_lens, out=None, workspace: Optional[Workspace] = None,
-                     softmax_scale: float = 0.0, debug_scores=None, debug_lse=None, stream=None):
+                     softmax_scale: float = 0.0, debug_scores=None, debug_lse=None, stream=None, tiles=None):
     """Attention only: returns the bf16 [B, Hq*D] head-major attention output."""
     torch = _check_dev("q", q, _torch().bfloat16)
     _check_dev("k_cache", k_cache, torch.bfloat16)
@@ -238,7 +264,7 @@ def decode_attn_only(q, k_cache, v_cache, seq_lens, out=None, workspace: Optiona
         out = torch.empty((B, Hq * D), dtype=torch.bfloat16, device=q.device)
     flags = DA_FLAG_DEBUG_SCORES if debug_scores is not None else 0
     shape = make_shape(B, Hq, Hkv, Lmax, 8, D, softmax_scale, flags=flags, debug_scores=_ptr(debug_scores),
-                       debug_lse=_ptr(debug_lse))
+                       debug_lse=_ptr(debug_lse), tiles=tiles)
     need = decode_attn_workspace_size(shape)
     ws = (workspace or Workspace(q.device)).get(need)
     shape.workspace = _ptr(ws)
@@ -296,10 +322,10 @@ class PreparedCall:
         return self.result
 
 
-def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what, flags=0):
+def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what, flags=0, tiles=None):
     B, Hq, D = q.shape
     _, Hkv, Lmax, _ = k_cache.shape
-    shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale, flags=flags)
+    shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale, flags=flags, tiles=tiles)
     need = decode_attn_workspace_size(shape)
     if need == 0:
         raise DecodeAttnError(DA_ERR_SHAPE, what)
@@ -310,7 +336,7 @@ def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what, flags=0):
 
 
 def DecodeStep(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Optional[Workspace] = None,
-               softmax_scale: float = 0.0, stream=None, separate=False) -> PreparedCall:
+               softmax_scale: float = 0.0, stream=None, separate=False, tiles=None) -> PreparedCall:
     """A prepared ``decode_attn_fwd``; calling it runs one decode step and returns ``out``."""
     torch = _check_dev("q", q, _torch().bfloat16)
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("o_weight", o_weight)):
@@ -319,7 +345,7 @@ def DecodeStep(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Opt
     if out is None:
         out = torch.empty((q.shape[0], o_weight.shape[1]), dtype=torch.bfloat16, device=q.device)
     shape, ws = _prepare_shape(q, k_cache, o_weight.shape[1], softmax_scale, workspace, "decode_attn_fwd",
-                               DA_FLAG_SEPARATE if separate else 0)
+                               DA_FLAG_SEPARATE if separate else 0, tiles)
     tensors = (q, k_cache, v_cache, seq_lens, o_weight, out)
     args = [ctypes.c_void_p(t.data_ptr()) for t in tensors] + [ctypes.byref(shape),
                                                               ctypes.c_void_p(_stream_handle(stream))]
@@ -327,7 +353,7 @@ def DecodeStep(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Opt
 
 
 def AttentionStep(q, k_cache, v_cache, seq_lens, out=None, workspace: Optional[Workspace] = None,
-                  softmax_scale: float = 0.0, stream=None) -> PreparedCall:
+                  softmax_scale: float = 0.0, stream=None, tiles=None) -> PreparedCall:
     """A prepared ``decode_attn_only``; calling it returns the bf16 [B, Hq*D] attention output."""
     torch = _check_dev("q", q, _torch().bfloat16)
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -336,7 +362,7 @@ def AttentionStep(q, k_cache, v_cache, seq_lens, out=None, workspace: Optional[W
     B, Hq, D = q.shape
     if out is None:
         out = torch.empty((B, Hq * D), dtype=torch.bfloat16, device=q.device)
-    shape, ws = _prepare_shape(q, k_cache, 8, softmax_scale, workspace, "decode_attn_only")
+    shape, ws = _prepare_shape(q, k_cache, 8, softmax_scale, workspace, "decode_attn_only", tiles=tiles)
     tensors = (q, k_cache, v_cache, seq_lens, out)
     args = [ctypes.c_void_p(t.data_ptr()) for t in tensors] + [ctypes.byref(shape),
                                                               ctypes.c_void_p(_stream_handle(stream))]

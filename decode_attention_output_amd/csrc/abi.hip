@@ -22,6 +22,7 @@ namespace {
 using da::kHeadDim;
 
 constexpr int kAttnWorkgroups = 256;        // stream-K attention: one per compute unit (longer ranges, fewer merges)
+constexpr int kMaxAttnWorkgroups = 1024;    // largest stream-K grid a tile override may ask for
 constexpr int kAttnBlockKeys = 32;          // keys per wave step
 constexpr int kTargetProjWorkgroups = 512;   // GEMV: two per compute unit
 constexpr int kTargetGemmWorkgroups = 512;   // MFMA GEMM: two per compute unit
@@ -38,6 +39,21 @@ int pow2_at_least(int x) {
 }
 bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
 
+// Ranges of a tile override (decode_attn_tiles_t); no override is always fine.
+bool tiles_ok(const decode_attn_shape_t* s) {
+  const decode_attn_tiles_t* t = s->tiles;
+  if (!t) return true;
+  if (t->attn_workgroups < 0 || t->attn_workgroups > kMaxAttnWorkgroups) return false;
+  if (t->attn_depth < 0 || t->attn_depth > 3) return false;
+  if (t->proj_ksplit < 0 || t->step_mode < 0 || t->step_mode > 2) return false;
+  if (const int tn = t->proj_tile_n) {
+    if (tn != 64 && tn != 128 && tn != 256 && tn != 512) return false;
+    if (s->batch < 16 && pow2_at_least(s->batch) * tn > 2048) return false;
+    if (s->batch >= 16 && tn != 64) return false;
+  }
+  return true;
+}
+
 bool shape_ok(const decode_attn_shape_t* s, bool need_hidden) {
   if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->max_seq_len < 1) return false;
   if (s->head_dim != kHeadDim) return false;
@@ -49,7 +65,7 @@ bool shape_ok(const decode_attn_shape_t* s, bool need_hidden) {
   // element counts must stay addressable
   const double kv = (double)s->batch * s->num_kv_heads * s->max_seq_len * kHeadDim;
   if (kv > 9.0e15) return false;
-  return true;
+  return tiles_ok(s);
 }
 
 // ---- projection tiles (shared by decode_attn_fwd and oproj_fwd) ----
@@ -62,21 +78,25 @@ struct ProjPlan {
   size_t part_bytes;
 };
 
-ProjPlan plan_proj(int M, int K, int N) {
+// A zero request keeps the built-in choice (tile_n and ksplit come from a
+// tile override, already range-checked by tiles_ok).
+ProjPlan plan_proj(int M, int K, int N, int tile_n_req = 0, int ksplit_req = 0) {
   ProjPlan pp{};
   if (M < 16) {
-    // GEMV: 64-column strips (a 128-byte line of each weight row per
-    // workgroup) and a K-chunk sized so that about kTargetProjWorkgroups
+    // GEMV: column tiles of up to 256 columns (512 bytes of each weight row
+    // per workgroup) and a K-chunk sized so that about kTargetProjWorkgroups
     // workgroups stream the weight; every lane keeps 8 rows in flight.
     pp.path = 0;
     pp.mpad = pow2_at_least(M);
     // widest tile (up to 256 columns) that still leaves 32 column tiles
     int tc = 256;
     while (tc > 64 && (N / tc < 32 || pp.mpad * tc > 2048)) tc /= 2;
+    if (tile_n_req) tc = tile_n_req;
     pp.tile_n = tc;
     pp.tiles = ceil_div(N, tc);
     const int gran = (2048 / tc) * kGemvUnroll;  // rows of one batch of the workgroup
     int ksplit = std::max(1, kTargetProjWorkgroups / pp.tiles);
+    if (ksplit_req) ksplit = ksplit_req;
     ksplit = std::min(ksplit, std::max(1, ceil_div(K, gran)));
     int kchunk = (int)align_up((size_t)ceil_div(K, ksplit), gran);
     // activations of a chunk + the reduction buffers fit 64 KiB of LDS
@@ -90,6 +110,7 @@ ProjPlan plan_proj(int M, int K, int N) {
     pp.tile_n = 64;
     pp.tiles = ceil_div(N, 64) * ceil_div(M, 16);
     int ksplit = std::max(1, kTargetGemmWorkgroups / pp.tiles);
+    if (ksplit_req) ksplit = ksplit_req;
     ksplit = std::min(ksplit, std::max(1, K / kGemmKStep));
     pp.kchunk = (int)align_up((size_t)ceil_div(K, ksplit), kGemmKStep);
     pp.ksplit = ceil_div(K, pp.kchunk);
@@ -101,6 +122,7 @@ ProjPlan plan_proj(int M, int K, int N) {
 // ---- attention: stream-K over the keys of all sequences ----
 struct AttnPlan {
   int gpad;
+  int depth;       // 32-key steps in flight per wave while one is computed
   int workgroups;  // stream-K workgroups
   int keys_per_wg; // upper bound of the keys one workgroup streams
   size_t slots;
@@ -116,6 +138,11 @@ AttnPlan plan_attn(const decode_attn_shape_t* s) {
   // about four blocks (128 keys) per workgroup at least: short problems are
   // latency bound and gain nothing from more, smaller pieces
   ap.workgroups = (int)std::max<long>(1, std::min<long>(kAttnWorkgroups, blocks_max / 4));
+  ap.depth = 1;
+  if (const decode_attn_tiles_t* t = s->tiles) {
+    if (t->attn_workgroups) ap.workgroups = (int)std::max<long>(1, std::min<long>(t->attn_workgroups, blocks_max));
+    if (t->attn_depth) ap.depth = t->attn_depth;
+  }
   ap.keys_per_wg = ceil_div(blocks_max, ap.workgroups) * kAttnBlockKeys;
   ap.slots = (size_t)ap.workgroups + (size_t)pairs;
   ap.part_o_bytes = align_up(ap.slots * G * kHeadDim * sizeof(float), kAlign);
@@ -221,7 +248,9 @@ Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
   int counters = s->batch * s->num_kv_heads;
   L.fused = false;
   if (with_proj) {
-    L.proj = plan_proj(s->batch, s->num_q_heads * kHeadDim, s->hidden);
+    const decode_attn_tiles_t* t = s->tiles;
+    L.proj = plan_proj(s->batch, s->num_q_heads * kHeadDim, s->hidden, t ? t->proj_tile_n : 0,
+                       t ? t->proj_ksplit : 0);
     L.off_flat = off;
     off += align_up((size_t)s->batch * s->num_q_heads * kHeadDim * sizeof(uint16_t), kAlign);
     L.off_proj_part = off;
@@ -233,7 +262,7 @@ Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
       const size_t step_total =
           da::kCounterBlockBytes + L.step.part_o_bytes + L.step.part_ml_bytes + L.step.proj_part_bytes;
       off = std::max(off, step_total);
-      L.fused = !(s->flags & DA_FLAG_SEPARATE);
+      L.fused = !(s->flags & DA_FLAG_SEPARATE) && !(t && t->step_mode == 2);
     }
   }
   L.total = off;
@@ -285,6 +314,7 @@ da::AttnParams attn_params(const void* q, const void* k, const void* v, const in
   p.G = s->num_q_heads / s->num_kv_heads;
   p.Lmax = s->max_seq_len;
   p.num_workgroups = L.attn.workgroups;
+  p.step_variant = L.attn.depth;
   const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;

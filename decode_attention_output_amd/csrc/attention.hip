@@ -10,7 +10,7 @@ namespace da {
 namespace {
 
 template <int GP, int NW, int D>
-__global__ __launch_bounds__(NW* kWave, 2) void attn_streamk_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW* kWave, D == 1 ? 2 : 1) void attn_streamk_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_streamk_lds<NW>()];
   attn_streamk_body<GP, NW, D>(p, blockIdx.x, gridDim.x, smem);
 }

@@ -18,7 +18,7 @@
 
 namespace da {
 
-constexpr int kMergeBatch = 16;  // partials whose loads are in flight together in the merge
+constexpr int kMergeBatch = 8;   // partials whose loads are in flight together in the merge
 
 // Block range [bound(i), bound(i+1)) of workgroup i of W over T blocks, and the
 // workgroup that owns block x. With T < W the first T workgroups take one

@@ -58,6 +58,33 @@ extern "C" {
                                    launches even where the plan would fuse them */
 
 /*
+ * Optional override of the tile choice for one call, for measured tile
+ * searches (the per-matmul sweep of the F-16 page, section 迭代过程). A zero
+ * field keeps the built-in choice; a value outside its range makes the call
+ * return DA_ERR_SHAPE.
+ *
+ *  attn_workgroups  stream-K attention workgroups, 1..1024 (capped at the
+ *                   number of 32-key blocks of the longest possible step)
+ *  attn_depth       32-key steps each attention wave has in flight while it
+ *                   computes one, 1..3
+ *  proj_tile_n      output columns per projection workgroup: 64, 128, 256 or
+ *                   512 (the GEMV for B < 16 also needs tile_n * B <= 2048 after
+ *                   B is rounded up to a power of two; the MFMA GEMM for
+ *                   B >= 16 takes 64, 128 or 256)
+ *  proj_ksplit      K-chunks the projection is cut into, >= 1 (rounded so that
+ *                   every chunk is a whole number of the kernel's row batches)
+ *  step_mode        0 built-in, 1 one launch where the single-launch step
+ *                   supports the shape, 2 two launches (as DA_FLAG_SEPARATE)
+ */
+typedef struct {
+  int32_t attn_workgroups;
+  int32_t attn_depth;
+  int32_t proj_tile_n;
+  int32_t proj_ksplit;
+  int32_t step_mode;
+} decode_attn_tiles_t;
+
+/*
  * Shape and per-call options of one decode step. All sizes in elements.
  *
  *  batch          B >= 1
@@ -79,6 +106,9 @@ extern "C" {
  *                 seq_lens[b]; other entries are left untouched
  *  debug_lse      with DA_FLAG_DEBUG_SCORES: device fp32 [B, Hq], natural log
  *                 of sum_j exp(score_j)
+ *  tiles          host pointer to a tile override, or NULL for the built-in
+ *                 choice; read during the call only. The workspace size
+ *                 depends on it.
  */
 typedef struct {
   int32_t batch;
@@ -93,6 +123,7 @@ typedef struct {
   uint32_t flags;
   float* debug_scores;
   float* debug_lse;
+  const decode_attn_tiles_t* tiles;
 } decode_attn_shape_t;
 
 /*

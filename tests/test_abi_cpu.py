@@ -179,3 +179,44 @@ def test_plan_fuses_small_steps_only(lib, cfg):
         # every workgroup of the single launch is resident at once (two per compute unit)
         assert plan.qk.workgroups + plan.oproj.workgroups <= 512
         assert plan.oproj_path == 0 and plan.oproj.tile_n in (128, 256, 512)
+
+
+@pytest.mark.parametrize("tiles", [dict(attn_workgroups=-1), dict(attn_workgroups=1025), dict(attn_depth=4),
+                                   dict(attn_depth=-2), dict(proj_tile_n=96), dict(proj_tile_n=1024),
+                                   dict(proj_ksplit=-1), dict(step_mode=3)])
+def test_tile_override_out_of_range_is_a_shape_error(lib, tiles):
+    shape = _shape(tiles=tiles)
+    assert da.decode_attn_workspace_size(shape) == 0
+    assert _fwd(lib, shape) == da.DA_ERR_SHAPE
+    with pytest.raises(da.DecodeAttnError):
+        da.decode_attn_plan(shape)
+
+
+def test_tile_override_gemv_width_limit(lib):
+    # the GEMV holds tile_n columns for every (power-of-two padded) row: at most 2048 values
+    assert da.decode_attn_workspace_size(_shape(batch=4, tiles=dict(proj_tile_n=512))) > 0
+    assert da.decode_attn_workspace_size(_shape(batch=5, tiles=dict(proj_tile_n=512))) == 0
+    # the MFMA GEMM (16 rows and more) has one column tile
+    assert da.decode_attn_workspace_size(_shape(batch=16, max_seq_len=8192, tiles=dict(proj_tile_n=128))) == 0
+
+
+def test_tile_override_reaches_the_plan(lib):
+    cfg = dict(batch=4, num_q_heads=64, num_kv_heads=8, max_seq_len=32768, hidden=8192)
+    base = da.decode_attn_plan(da.make_shape(**cfg))
+    over = da.decode_attn_plan(da.make_shape(tiles=dict(attn_workgroups=192, proj_tile_n=128, proj_ksplit=8), **cfg))
+    assert base.qk.workgroups != 192 and over.qk.workgroups == 192
+    assert over.num_splits == 192 and over.split_len * 192 >= 4 * 8 * 32768
+    assert over.oproj.tile_n == 128 and over.oproj.split == 8
+    assert over.oproj.workgroups == (8192 // 128) * 8
+    # zero fields keep the built-in choice
+    same = da.decode_attn_plan(da.make_shape(tiles={}, **cfg))
+    assert (same.qk.workgroups, same.oproj.tile_n, same.oproj.split) == (base.qk.workgroups, base.oproj.tile_n,
+                                                                         base.oproj.split)
+    # a grid wider than the blocks of the step is capped at one 32-key block per workgroup
+    tiny = da.decode_attn_plan(da.make_shape(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=256, hidden=512,
+                                             tiles=dict(attn_workgroups=1024, step_mode=2)))
+    assert tiny.fused == 0 and tiny.qk.workgroups == 8
+    # step_mode 2 asks for two launches where the built-in choice fuses
+    pages = dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=2048, hidden=4096)
+    assert da.decode_attn_plan(da.make_shape(**pages)).fused == 1
+    assert da.decode_attn_plan(da.make_shape(tiles=dict(step_mode=2), **pages)).fused == 0

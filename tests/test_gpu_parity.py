@@ -264,3 +264,30 @@ def test_oproj_random(gpu, shape):
     out = host_words(da.oproj_fwd(dev_bf16(x), dev_bf16(w)))
     _, ref = oracle.oproj(x, w)
     assert_bf16_close(out, ref, "oproj %s" % (shape,))
+
+
+# ---- tile overrides (the measured tile search runs through them) ---------
+
+TILES = [
+    dict(attn_workgroups=1), dict(attn_workgroups=7, attn_depth=2), dict(attn_workgroups=192, attn_depth=3),
+    dict(attn_workgroups=1024), dict(attn_depth=2, proj_tile_n=64, proj_ksplit=1),
+    dict(proj_tile_n=128, proj_ksplit=3), dict(proj_tile_n=256, proj_ksplit=64), dict(step_mode=2),
+]
+
+
+@pytest.mark.parametrize("tiles", TILES, ids=lambda t: "-".join("%s%d" % (k, v) for k, v in t.items()))
+@pytest.mark.parametrize("B", [3, 17])
+def test_tile_overrides_match_the_oracle(gpu, tiles, B):
+    if B >= 16 and tiles.get("proj_tile_n", 64) != 64:
+        pytest.skip("the MFMA projection has one column tile")
+    sl = [int(x) for x in np.random.default_rng(B).integers(1, 3000, size=B)]
+    inp = workloads.custom_decode_inputs(B, 16, 4, sl, max_seq_len=3000, hidden=520, seed=300 + B)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    s, w = dev_i32(inp["seq_lens"]), dev_bf16(inp["o_weight"])
+    ws = da.Workspace()
+    flat = host_words(da.decode_attn_only(q, k, v, s, workspace=ws, tiles=tiles))
+    out = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, tiles=tiles))
+    _counter_block_is_clear(ws)
+    again = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, tiles=tiles))
+    np.testing.assert_array_equal(out, again)
+    _check_step(inp, {"flat": flat, "out": out}, what="tiles %s" % (tiles,))
