@@ -50,7 +50,7 @@ def kernel_source_hash() -> str:
 def traffic_from_profile(workload: str, kernel_prefix: str):
     """Measured HBM bytes per dispatch of the dominant kernel, from the committed
     rocprofv3 PMC summary of this workload, if it was taken on the current sources."""
-    path = os.path.join(PROFILES, "pmc_%s.txt" % workload)
+    path = os.path.join(PROFILES, "%s_%s.txt" % (kernel_prefix, workload))
     if not os.path.exists(path):
         return None
     fields = {}
@@ -91,7 +91,7 @@ def dominant_kernel(wl, plan, seq_lens):
 
 
 def summarize_profile(args):
-    """profiles/pmc_<workload>.txt from a FETCH_SIZE run, a WRITE_SIZE run and a kernel-trace run."""
+    """profiles/<kernel>_<workload>.txt from a FETCH_SIZE run, a WRITE_SIZE run and a kernel-trace run."""
     import csv
 
     import decode_attention_output_amd as da
@@ -128,7 +128,7 @@ def summarize_profile(args):
             stats.append((row["Name"], int(row["Calls"]), float(row["AverageNs"]), float(row["MinNs"]),
                           float(row["MaxNs"])))
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, "pmc_%s.txt" % wl.name)
+    out = os.path.join(PROFILES, "%s_%s.txt" % (kname, wl.name))
     with open(out, "w") as f:
         f.write("# rocprofv3 summary: %s, workload %s\n" % (kname, wl.name))
         f.write("# commands (run from the repository root on one MI355X):\n")
@@ -170,7 +170,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=workloads.PAGES.name, choices=[w.name for w in workloads.DECODE])
     ap.add_argument("--min-rotate-mib", type=float, default=512.0)
-    ap.add_argument("--breakdown-steps", type=int, default=200, help="launches per kernel in the breakdown pass")
+    ap.add_argument("--breakdown-steps", type=int, default=400, help="launches per kernel in the breakdown pass")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -268,30 +268,29 @@ def main():
         graph_us = gv0.elapsed_time(gv1) * 1e3 / args.steps
         del g
 
-    # ---- per-kernel pass: the attention launch and the projection launch ----
+    # ---- per-kernel pass: the attention launch alone and the projection launch alone ----
+    # Each is timed like the step: n_b back-to-back launches on the bench stream between
+    # two HIP events, cycling through the rotation sets; the average per launch is the
+    # kernel's launch duration (the rocprofv3 kernel trace of the same command agrees).
     n_b = args.breakdown_steps
-    ev_a = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_b)]
-    ev_o = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_b)]
-    ev_s = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_b)]
-    for i in range(n_b):
-        ev_s[i][0].record(stream)
-        sets[i % R]["step"]()
-        ev_s[i][1].record(stream)
     for st in sets:
         st["attn"] = da.AttentionStep(st["q"], st["k"], st["v"], sl, out=st["flat"], workspace=st["ws"], stream=stream)
         st["proj"] = da.OprojStep(st["flat"], st["o_weight"], out=st["out"], workspace=st["ws"], stream=stream)
-    for i in range(n_b):
-        ev_a[i][0].record(stream)
-        sets[i % R]["attn"]()
-        ev_a[i][1].record(stream)
-    for i in range(n_b):
-        ev_o[i][0].record(stream)
-        sets[i % R]["proj"]()
-        ev_o[i][1].record(stream)
-    torch.cuda.synchronize()
-    attn_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev_a)
-    oproj_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev_o)
-    step_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev_s)
+
+    def avg_launch_us(name):
+        for i in range(min(R, 10)):
+            sets[i % R][name]()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n_b):
+            sets[i % R][name]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n_b
+
+    attn_us = avg_launch_us("attn")
+    oproj_us = avg_launch_us("proj")
+    step_us = gpu_us  # the timed region above
     # restore the step's own output in set 0 for the parity check
     sets[0]["step"]()
     torch.cuda.synchronize()
@@ -344,10 +343,12 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(dom_us, 3),
             "alg_bytes_per_launch": kbytes,
-            "timing": "median of %d HIP-event pairs around single launches on the bench stream" % n_b,
+            "timing": ("HIP events around the timed steps (one launch each) on the bench stream" if which == "step"
+                       else "HIP events around %d back-to-back launches of this kernel alone on the bench stream"
+                       % n_b),
         },
-        "breakdown_us": {"step_single_launch": round(step_us, 3), "attention": round(attn_us, 3),
-                         "oproj": round(oproj_us, 3)},
+        "breakdown_us": {"step": round(step_us, 3), "attention_alone": round(attn_us, 3),
+                         "oproj_alone": round(oproj_us, 3)},
     }
 
     if not args.no_parity or not args.no_cpu_baseline:

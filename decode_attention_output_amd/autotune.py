@@ -10,7 +10,8 @@ tool does that search on the GPU through the C ABI's tile override
      timed with decode_attn_only;
   2. projection (attn_output_flat x o_weight): column tile x K split, timed as
      the whole step in two launches with the best attention tiles;
-  3. one launch against two, where the single-launch step supports the shape.
+  3. where the single-launch step supports the shape: its attention pieces x
+     projection column tile, against two launches.
 
 Every candidate is timed over rotated copies of the inputs (at least 512 MiB,
 twice the Infinity Cache) with HIP events on one stream, median of several
@@ -49,6 +50,8 @@ def parse(argv=None):
     ap.add_argument("--launches", type=int, default=100, help="timed launches per repeat")
     ap.add_argument("--repeats", type=int, default=5)
     ap.add_argument("--min-rotate-mib", type=float, default=512.0)
+    ap.add_argument("--step-wgs", default="32,64,96,128,192,256",
+                    help="attention workgroups aimed at in the single-launch step")
     ap.add_argument("--skip", default="", help="comma list of stages to skip: attn,proj,mode")
     return ap.parse_args(argv)
 
@@ -170,10 +173,12 @@ def main(argv=None):
     best, best_us = best_proj, best_proj_us
     plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden))
     if "mode" not in skip and plan.fused:
-        t = {"step_mode": 1}
-        us = try_tiles("mode", t, step_calls, ref_out, "out", alg_bytes)
-        if us is not None and us < best_us:
-            best, best_us = t, us
+        # the single-launch step: attention workgroups aimed at x projection column tile
+        for w, tn in itertools.product([0] + _parse_list(args.step_wgs), [0, 128, 256, 512]):
+            t = {"step_mode": 1, "attn_workgroups": w, "proj_tile_n": tn}
+            us = try_tiles("mode", t, step_calls, ref_out, "out", alg_bytes)
+            if us is not None and us < best_us:
+                best, best_us = t, us
     builtin_us = try_tiles("builtin", {}, step_calls, ref_out, "out", alg_bytes)
     print(json.dumps({"workload": wl.name, "best": best, "best_us": round(best_us, 3),
                       "builtin_us": None if builtin_us is None else round(builtin_us, 3),

@@ -108,50 +108,64 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
     *reinterpret_cast<uint2*>(p.flat + ((size_t)b * p.Hq + qh) * kHeadDim + d4 * 4) = make_uint2(w01, w23);
   };
 
-  while (x < xe) {
-    // ---- the sequence (b, h) that block x belongs to ----
+  // ---- the piece that starts at block y: its sequence (b, h) and block range ----
+  struct Piece {
+    int b, h, seg, L;
+    int lb0, lb1;     // blocks [lb0, lb1) of the sequence
+    long ss, se, pe;  // the sequence's first and end block, the piece's end block (flattened)
+    bool whole;
+  };
+  auto piece_at = [&](long y) {
+    Piece pc;
     int lo = 0, hi = B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if ((long)Hkv * uniform(s_pre[mid]) <= x) lo = mid; else hi = mid;
+      if ((long)Hkv * uniform(s_pre[mid]) <= y) lo = mid; else hi = mid;
     }
-    const int b = lo;
-    const int pre_b = uniform(s_pre[b]);
-    const int nb = uniform(s_pre[b + 1]) - pre_b;
+    pc.b = lo;
+    const int pre_b = uniform(s_pre[pc.b]);
+    const int nb = uniform(s_pre[pc.b + 1]) - pre_b;
     const long seg0 = (long)Hkv * pre_b;
-    const int h = (int)((x - seg0) / nb);
-    const long ss = seg0 + (long)h * nb, se = ss + nb;
-    const long pe = min(xe, se);
-    const int lb0 = (int)(x - ss), lb1 = (int)(pe - ss);
-    const bool whole = (x == ss && pe == se);
-    const int seg = b * Hkv + h;
-    const int L = uniform(s_len[b]);
-
+    pc.h = (int)((y - seg0) / nb);
+    pc.ss = seg0 + (long)pc.h * nb;
+    pc.se = pc.ss + nb;
+    pc.pe = min(xe, pc.se);
+    pc.lb0 = (int)(y - pc.ss);
+    pc.lb1 = (int)(pc.pe - pc.ss);
+    pc.whole = (y == pc.ss && pc.pe == pc.se);
+    pc.seg = pc.b * Hkv + pc.h;
+    pc.L = uniform(s_len[pc.b]);
+    return pc;
+  };
+  auto seg_of = [&](const Piece& pc) {
     AttnSeg sg;
-    const size_t kv_off = (size_t)seg * p.Lmax * kHeadDim;
-    sg.K = make_rsrc(p.k + kv_off, (uint32_t)L * kRowBytes);
-    sg.V = make_rsrc(p.v + kv_off, (uint32_t)L * kRowBytes);
-    sg.L = L;
+    const size_t kv_off = (size_t)pc.seg * p.Lmax * kHeadDim;
+    sg.K = make_rsrc(p.k + kv_off, (uint32_t)pc.L * kRowBytes);
+    sg.V = make_rsrc(p.v + kv_off, (uint32_t)pc.L * kRowBytes);
+    sg.L = pc.L;
     sg.G = G;
     sg.scale_log2 = p.scale_log2;
     sg.scale = p.scale;
-    sg.dbg = p.dbg_scores ? p.dbg_scores + ((size_t)b * p.Hq + (size_t)h * G) * p.Lmax : nullptr;
+    sg.dbg = p.dbg_scores ? p.dbg_scores + ((size_t)pc.b * p.Hq + (size_t)pc.h * G) * p.Lmax : nullptr;
     sg.dbg_stride = p.Lmax;
+    return sg;
+  };
+  auto query_of = [&](uint4 (&qa)[4], const Piece& pc) {
+    load_query(qa, p.q + ((size_t)pc.b * p.Hq + (size_t)pc.h * G) * kHeadDim, G, col, grp);
+  };
+  // this wave's 32-key steps of a piece: the piece's keys [lb0*32, min(lb1*32, L)),
+  // interleaved over the waves; every step holds at least one key of the sequence
+  auto wave_steps = [&](const Piece& pc) {
+    const int nstep = (min(pc.lb1 * kBlockKeys, pc.L) - pc.lb0 * kBlockKeys + kStepKeys - 1) / kStepKeys;
+    return nstep > wave ? (nstep - wave + NW - 1) / NW : 0;
+  };
 
-    uint4 qa[4];
-    load_query(qa, p.q + ((size_t)b * p.Hq + (size_t)h * G) * kHeadDim, G, col, grp);
-    AttnWave aw;
-    aw.reset();
-    // the piece's keys [lb0*32, min(lb1*32, L)) in 32-key steps, interleaved over the
-    // waves; every step holds at least one key of the sequence
-    const int nstep = (min(lb1 * kBlockKeys, L) - lb0 * kBlockKeys + kStepKeys - 1) / kStepKeys;
-    const int n = nstep > wave ? (nstep - wave + NW - 1) / NW : 0;
-    attn_wave_steps<GP, D>(aw, qa, sg, lb0 + wave, NW, n, L, s_stage + wave * kStageBytes, lane);
+  // ---- the end of a piece: merge the waves, then write the sequence's output or store a partial ----
+  auto finish_piece = [&](const Piece& pc, AttnWave& aw) {
+    const int b = pc.b, h = pc.h, seg = pc.seg;
     attn_wave_to_lds<GP>(aw, s_o(wave), s_m(wave), s_l(wave), lane);
     __syncthreads();
     DA_TRACE(2);
-
-    // ---- merge the waves: the whole sequence, or one partial of it ----
     const int slot = seg + (int)wg;
     for (int idx = t; idx < G * 32; idx += NT) {
       const int g = idx >> 5, d4 = idx & 31;
@@ -170,7 +184,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
         O[3] = fmaf(f, o4.w, O[3]);
       }
       const int qh = h * G + g;
-      if (whole) {
+      if (pc.whole) {
         store4(b, qh, d4, O, 1.f / Ls);
         if (p.dbg_lse && d4 == 0) p.dbg_lse[(size_t)b * p.Hq + qh] = (M + log2f(Ls)) * kLn2;
       } else {
@@ -183,10 +197,10 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
       }
     }
 
-    if (!whole) {
+    if (!pc.whole) {
       // (the barrier inside arrive_last_coherent also ends the reads of the waves' outputs,
       // whose bytes the merge scratch reuses)
-      const long first = range_owner(ss, T, W), last = range_owner(se - 1, T, W);
+      const long first = range_owner(pc.ss, T, W), last = range_owner(pc.se - 1, T, W);
       const int P = (int)(last - first + 1);
       const bool last_piece = arrive_last_coherent(&p.counters[seg], (uint32_t)P);
       DA_TRACE(3);
@@ -243,7 +257,18 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
       }
     }
     __syncthreads();  // LDS is reused by the next piece
-    x = pe;
+  };
+
+  while (x < xe) {
+    const Piece pc = piece_at(x);
+    const AttnSeg sg = seg_of(pc);
+    uint4 qa[4];
+    query_of(qa, pc);
+    AttnWave aw;
+    aw.reset();
+    attn_wave_steps<GP, D>(aw, qa, sg, pc.lb0 + wave, NW, wave_steps(pc), pc.L, s_stage + wave * kStageBytes, lane);
+    finish_piece(pc, aw);
+    x = pc.pe;
   }
   DA_TRACE(6);
 }

@@ -126,16 +126,16 @@ __device__ __forceinline__ void gemv_finish(const GemvParams& p, float (&acc)[MB
 // One GEMV work item: a TC-column tile of the weight (TC*2 bytes of every row)
 // times a K-chunk of rows. Lane t streams 16-byte pieces of rows rr, rr+RPP,
 // ... (rr = t/(TC/8)) of column group t%(TC/8), a batch of kGemvUnroll rows at
-// a time with the next batch in flight while the current one is multiplied.
-// `before_x()` runs (in every thread) after the first weight batch has been
-// requested and before the activation chunk is read; the activations are
-// staged in LDS as fp32 (`s_x`: kchunk * MB floats) and, with COHERENT_X, read
-// with device-coherent loads (they were written earlier in the same launch).
+// a time. The activation chunk (a few KiB) is requested first, then the first
+// two weight batches, so that the activations arrive ahead of the weight
+// stream (loads of one wave complete in order) and two batches are in flight
+// while the activations are staged in LDS as fp32 (`s_x`: kchunk * MB floats).
+// After that one batch is multiplied while the next is in flight.
 constexpr int kGemvUnroll = 8;
+constexpr int kGemvXRegs = 8;  // activation loads (8 bytes) a lane holds before the weight requests
 
-template <int MB, int TC, bool COHERENT_X, class BeforeX>
-__device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int ks, float* s_x, char* fin_smem,
-                                          BeforeX before_x) {
+template <int MB, int TC>
+__device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int ks, float* s_x, char* fin_smem) {
   constexpr int kLanesPerRow = TC / 8;
   constexpr int kRowLanes = kGemvThreads / kLanesPerRow;
   const int n0 = tile * TC;
@@ -177,33 +177,41 @@ __device__ __forceinline__ void gemv_item(const GemvParams& p, int tile, int ks,
     }
   };
 
-  uint4 wa[kGemvUnroll], wb[kGemvUnroll];
-  load_batch(wa, 0);
-  before_x();
-  // activations in groups of 4 (K and the chunk are multiples of 8)
+  // activations in groups of 4 (K and the chunk are multiples of 8): element idx
+  // of the chunk is row m = idx / (kn/4), columns 4*(idx % (kn/4)) .. +4
   const rsrc_t xr = make_rsrc(p.x, (uint32_t)min((size_t)p.M * p.K * 2, (size_t)0x7fffffff));
-  for (int idx = t; idx < MB * (kn / 4); idx += kGemvThreads) {
+  const int nx = MB * (kn / 4);
+  auto x_load = [&](int idx) {
     const int m = idx / (kn / 4), k4 = idx % (kn / 4);
-    uint2 v = make_uint2(0, 0);
-    if (m < p.M) {
-      const uint32_t off = (uint32_t)(((size_t)m * p.K + k0 + 4 * k4) * 2);
-      if constexpr (COHERENT_X)
-        v = rsrc_ld8_coherent(xr, off);
-      else
-        v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(xr, (int)off, 0, 0));
-    }
+    if (idx >= nx || m >= p.M) return make_uint2(0, 0);
+    const uint32_t off = (uint32_t)(((size_t)m * p.K + k0 + 4 * k4) * 2);
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(xr, (int)off, 0, 0));
+  };
+  auto x_store = [&](int idx, uint2 v) {
+    if (idx >= nx) return;
+    const int m = idx / (kn / 4), k4 = idx % (kn / 4);
     s_x[(4 * k4 + 0) * MB + m] = bf16_lo(v.x);
     s_x[(4 * k4 + 1) * MB + m] = bf16_hi(v.x);
     s_x[(4 * k4 + 2) * MB + m] = bf16_lo(v.y);
     s_x[(4 * k4 + 3) * MB + m] = bf16_hi(v.y);
-  }
+  };
+  uint2 xv[kGemvXRegs];
+#pragma unroll
+  for (int j = 0; j < kGemvXRegs; ++j) xv[j] = x_load(t + j * kGemvThreads);
+
+  uint4 wa[kGemvUnroll], wb[kGemvUnroll];
+  load_batch(wa, 0);
+  if (nbatch > 1) load_batch(wb, 1);
+#pragma unroll
+  for (int j = 0; j < kGemvXRegs; ++j) x_store(t + j * kGemvThreads, xv[j]);
+  for (int idx = t + kGemvXRegs * kGemvThreads; idx < nx; idx += kGemvThreads) x_store(idx, x_load(idx));
   __syncthreads();
   for (int bt = 0; bt < nbatch; bt += 2) {
-    if (bt + 1 < nbatch) load_batch(wb, bt + 1);
     use_batch(wa, bt);
-    if (bt + 1 >= nbatch) break;
     if (bt + 2 < nbatch) load_batch(wa, bt + 2);
+    if (bt + 1 >= nbatch) break;
     use_batch(wb, bt + 1);
+    if (bt + 3 < nbatch) load_batch(wb, bt + 3);
   }
   gemv_finish<MB, TC>(p, acc, tile, ks, &p.counters[tile], fin_smem);
 }

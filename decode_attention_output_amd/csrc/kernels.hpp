@@ -54,17 +54,21 @@ struct GemvParams {
   int tile_n;         // output columns per workgroup (64)
 };
 
-// C[M, N] = A[M, K] @ B[K, N] on MFMA, 16 x 64 output tile per workgroup.
+// C[M, N] = A[M, K] @ B[K, N] on MFMA, a (16 * mtiles) x 128 output tile per
+// workgroup; K and kchunk are multiples of 32, N of 8.
 struct GemmParams {
   const uint16_t* a;  // [M, K]
   const uint16_t* b;  // [K, N]
   uint16_t* c;        // [M, N]
   float* part;        // fp32 [ksplit, M, N] (ksplit > 1)
   uint32_t part_bytes;
-  uint32_t* counters; // [ceil(M/16) * N/64] arrival counters (ksplit > 1)
+  uint32_t* counters; // [ceil(M / (16 * mtiles)) * ceil(N / 128)] arrival counters (ksplit > 1)
   int M, K, N;
   int kchunk, ksplit;
+  int mtiles;         // 16-row m-tiles per workgroup: 1, 2 or 4
 };
+constexpr int kGemmTileN = 128;   // output columns per GEMM workgroup
+constexpr int kGemmDepth = 2;     // 32-row steps per wave in flight while one is multiplied
 
 hipError_t launch_attention(const AttnParams& p, int gpad, hipStream_t s);
 // The single-launch decode step for small steps (a few tokens, a few thousand

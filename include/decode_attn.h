@@ -64,13 +64,17 @@ extern "C" {
  * return DA_ERR_SHAPE.
  *
  *  attn_workgroups  stream-K attention workgroups, 1..1024 (capped at the
- *                   number of 32-key blocks of the longest possible step)
+ *                   number of 32-key blocks of the longest possible step); in
+ *                   the single-launch step, the attention workgroups aimed at
+ *                   (every sequence is cut into the same number of pieces)
  *  attn_depth       32-key steps each attention wave has in flight while it
  *                   computes one, 1..3
  *  proj_tile_n      output columns per projection workgroup: 64, 128, 256 or
  *                   512 (the GEMV for B < 16 also needs tile_n * B <= 2048 after
  *                   B is rounded up to a power of two; the MFMA GEMM for
- *                   B >= 16 takes 64, 128 or 256)
+ *                   B >= 16 takes 128 only; the single-launch step takes 128,
+ *                   256 or 512 and falls back to two launches if the shape
+ *                   does not fit that tile)
  *  proj_ksplit      K-chunks the projection is cut into, >= 1 (rounded so that
  *                   every chunk is a whole number of the kernel's row batches)
  *  step_mode        0 built-in, 1 one launch where the single-launch step
@@ -197,7 +201,8 @@ int oproj_fwd(const void* x_dev, const void* w_dev, void* out_dev, int32_t M, in
 /*
  * Dense GEMM of the CANN msKPP BasicMatmul example ("自动调优流程 / Kernel级
  * 自动调优"): C[M,N] = A[M,K] @ B[K,N], all fp16 row-major, fp32 accumulation,
- * fp16 out (round to nearest even). M, N multiples of 16; K a multiple of 32.
+ * fp16 out (round to nearest even). M, N multiples of 16; K a multiple of 32;
+ * K * N * 2 < 4 GiB (DA_ERR_SHAPE otherwise).
  */
 int gemm_f16(const void* a_dev, const void* b_dev, void* c_dev, int32_t M, int32_t N, int32_t K, void* stream);
 

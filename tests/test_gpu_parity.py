@@ -278,7 +278,7 @@ TILES = [
 @pytest.mark.parametrize("tiles", TILES, ids=lambda t: "-".join("%s%d" % (k, v) for k, v in t.items()))
 @pytest.mark.parametrize("B", [3, 17])
 def test_tile_overrides_match_the_oracle(gpu, tiles, B):
-    if B >= 16 and tiles.get("proj_tile_n", 64) != 64:
+    if B >= 16 and tiles.get("proj_tile_n", 128) != 128:
         pytest.skip("the MFMA projection has one column tile")
     sl = [int(x) for x in np.random.default_rng(B).integers(1, 3000, size=B)]
     inp = workloads.custom_decode_inputs(B, 16, 4, sl, max_seq_len=3000, hidden=520, seed=300 + B)
