@@ -17,10 +17,12 @@ Every candidate is timed over rotated copies of the inputs (at least 512 MiB,
 twice the Infinity Cache) with HIP events on one stream, median of several
 repeats, and its output is compared with the built-in choice's output (two
 correct results differ by at most a couple of bf16 ulps). The result is one
-JSON line per candidate and a final line with the best tiles, in the form of
-a row of the built-in tile table (csrc/tile_table.hpp).
+JSON line per candidate and a final line with the best tiles; with --emit the
+best tiles become the shape's row of the measured tile table
+(csrc/tile_table.inc), which the library consults for calls without an
+override of their own (rebuild after emitting).
 
-    python -m decode_attention_output_amd.autotune --workload decode_b4_h64kv8_L32768_o8192
+    python -m decode_attention_output_amd.autotune --workload decode_b4_h64kv8_L32768_o8192 --emit
 """
 from __future__ import annotations
 
@@ -53,7 +55,32 @@ def parse(argv=None):
     ap.add_argument("--step-wgs", default="32,64,96,128,192,256",
                     help="attention workgroups aimed at in the single-launch step")
     ap.add_argument("--skip", default="", help="comma list of stages to skip: attn,proj,mode")
+    ap.add_argument("--emit", action="store_true", help="write the best tiles into csrc/tile_table.inc")
+    ap.add_argument("--table", default=TABLE, help=argparse.SUPPRESS)
     return ap.parse_args(argv)
+
+
+TABLE = os.path.join(HERE, "csrc", "tile_table.inc")
+TILE_FIELDS = ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit", "step_mode")
+
+
+def emit_entry(path, shape, tiles, note):
+    """Insert or replace the table row of `shape` (a dict of batch, num_q_heads, num_kv_heads,
+    max_seq_len, hidden); the header comment and the other rows are kept, rows sorted by shape."""
+    key = (shape["batch"], shape["num_q_heads"], shape["num_kv_heads"], shape["max_seq_len"], shape["hidden"])
+    head, rows = [], {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("TILE_ENTRY("):
+                vals = [int(v) for v in line[len("TILE_ENTRY("):line.index(")")].split(",")]
+                rows[tuple(vals[:5])] = line
+            else:
+                head.append(line)
+    vals = list(key) + [int(tiles.get(n, 0)) for n in TILE_FIELDS]
+    rows[key] = "TILE_ENTRY(%s)  // %s\n" % (", ".join(str(v) for v in vals), note)
+    with open(path, "w") as f:
+        f.writelines(head)
+        f.writelines(rows[k] for k in sorted(rows))
 
 
 def main(argv=None):
@@ -180,10 +207,14 @@ def main(argv=None):
             if us is not None and us < best_us:
                 best, best_us = t, us
     builtin_us = try_tiles("builtin", {}, step_calls, ref_out, "out", alg_bytes)
+    shape = {"batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+             "max_seq_len": s.max_seq_len, "hidden": s.hidden}
     print(json.dumps({"workload": wl.name, "best": best, "best_us": round(best_us, 3),
-                      "builtin_us": None if builtin_us is None else round(builtin_us, 3),
-                      "shape": {"batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
-                                "max_seq_len": s.max_seq_len, "hidden": s.hidden}}), flush=True)
+                      "builtin_us": None if builtin_us is None else round(builtin_us, 3), "shape": shape}),
+          flush=True)
+    if args.emit:
+        emit_entry(args.table, shape, best, "%s: %.2f us (built-in %s us)" % (
+            wl.name, best_us, "?" if builtin_us is None else "%.2f" % builtin_us))
 
 
 if __name__ == "__main__":

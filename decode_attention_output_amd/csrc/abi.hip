@@ -43,6 +43,32 @@ int pow2_at_least(int x) {
 }
 bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
 
+// ---- the measured tile table (tile_table.inc, written by autotune.py) ----
+struct TileEntry {
+  int32_t B, Hq, Hkv, Lmax, N;
+  decode_attn_tiles_t tiles;
+};
+constexpr TileEntry kTileTable[] = {
+#define TILE_ENTRY(b, hq, hkv, lmax, n, w, d, tn, ks, mode) {b, hq, hkv, lmax, n, {w, d, tn, ks, mode}},
+#include "tile_table.inc"
+#undef TILE_ENTRY
+    {0, 0, 0, 0, 0, {0, 0, 0, 0, 0}},  // end of the table
+};
+
+// The shape a call runs with: the caller's, plus the table's tiles for its
+// exact shape when the caller brings no override.
+decode_attn_shape_t effective_shape(const decode_attn_shape_t* s) {
+  decode_attn_shape_t e = *s;
+  if (e.tiles) return e;
+  for (const TileEntry& t : kTileTable)
+    if (t.B == e.batch && t.Hq == e.num_q_heads && t.Hkv == e.num_kv_heads && t.Lmax == e.max_seq_len &&
+        t.N == e.hidden && t.B > 0) {
+      e.tiles = &t.tiles;
+      break;
+    }
+  return e;
+}
+
 // Ranges of a tile override (decode_attn_tiles_t); no override is always fine.
 bool tiles_ok(const decode_attn_shape_t* s) {
   const decode_attn_tiles_t* t = s->tiles;
@@ -429,14 +455,19 @@ int run_step(const void* q, const void* k, const void* v, const int32_t* sl, con
 
 extern "C" {
 
-size_t decode_attn_workspace_size(const decode_attn_shape_t* shape) {
-  if (!shape || !shape_ok(shape, true)) return 0;
+size_t decode_attn_workspace_size(const decode_attn_shape_t* shape_in) {
+  if (!shape_in) return 0;
+  const decode_attn_shape_t eff = effective_shape(shape_in);
+  const decode_attn_shape_t* shape = &eff;
+  if (!shape_ok(shape, true)) return 0;
   const Layout L = layout_for(shape, true);
   return L.fits ? L.total : 0;
 }
 
-int decode_attn_plan(const decode_attn_shape_t* shape, decode_attn_plan_t* plan) {
-  if (!shape || !plan) return DA_ERR_NULL;
+int decode_attn_plan(const decode_attn_shape_t* shape_in, decode_attn_plan_t* plan) {
+  if (!shape_in || !plan) return DA_ERR_NULL;
+  const decode_attn_shape_t eff = effective_shape(shape_in);
+  const decode_attn_shape_t* shape = &eff;
   if (!shape_ok(shape, true)) return DA_ERR_SHAPE;
   const Layout L = layout_for(shape, true);
   if (!L.fits) return DA_ERR_SHAPE;
@@ -473,8 +504,10 @@ int decode_attn_plan(const decode_attn_shape_t* shape, decode_attn_plan_t* plan)
 }
 
 int decode_attn_fwd(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                    const void* o_weight, void* out, const decode_attn_shape_t* shape, void* stream) {
-  if (!shape) return DA_ERR_NULL;
+                    const void* o_weight, void* out, const decode_attn_shape_t* shape_in, void* stream) {
+  if (!shape_in) return DA_ERR_NULL;
+  const decode_attn_shape_t eff = effective_shape(shape_in);
+  const decode_attn_shape_t* shape = &eff;
   int rc = check_attn_ptrs(q, k_cache, v_cache, seq_lens, out);
   if (rc) return rc;
   if (!o_weight) return DA_ERR_NULL;
@@ -495,8 +528,10 @@ int decode_attn_fwd(const void* q, const void* k_cache, const void* v_cache, con
 }
 
 int decode_attn_only(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                     void* attn_out, const decode_attn_shape_t* shape, void* stream) {
-  if (!shape) return DA_ERR_NULL;
+                     void* attn_out, const decode_attn_shape_t* shape_in, void* stream) {
+  if (!shape_in) return DA_ERR_NULL;
+  const decode_attn_shape_t eff = effective_shape(shape_in);
+  const decode_attn_shape_t* shape = &eff;
   int rc = check_attn_ptrs(q, k_cache, v_cache, seq_lens, attn_out);
   if (rc) return rc;
   if (!shape_ok(shape, false)) return DA_ERR_SHAPE;

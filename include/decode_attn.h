@@ -111,8 +111,9 @@ typedef struct {
  *  debug_lse      with DA_FLAG_DEBUG_SCORES: device fp32 [B, Hq], natural log
  *                 of sum_j exp(score_j)
  *  tiles          host pointer to a tile override, or NULL for the built-in
- *                 choice; read during the call only. The workspace size
- *                 depends on it.
+ *                 choice (the measured tile table's row for this exact shape
+ *                 if it has one, else the built-in rules); read during the
+ *                 call only. The workspace size depends on it.
  */
 typedef struct {
   int32_t batch;

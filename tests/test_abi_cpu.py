@@ -175,7 +175,8 @@ def test_plan_fuses_small_steps_only(lib, cfg):
     assert sep.fused == 0
     # the workspace does not depend on the launch choice
     assert plan.workspace_bytes == sep.workspace_bytes
-    assert (sep.qk.workgroups, sep.split_len) == (plan.qk.workgroups, plan.split_len)
+    if not plan.fused:
+        assert (sep.qk.workgroups, sep.split_len) == (plan.qk.workgroups, plan.split_len)
     if plan.fused:
         # every workgroup of the single launch is resident at once (two per compute unit)
         assert plan.qk.workgroups + plan.oproj.workgroups <= 512
@@ -221,3 +222,26 @@ def test_tile_override_reaches_the_plan(lib):
     pages = dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=2048, hidden=4096)
     assert da.decode_attn_plan(da.make_shape(**pages)).fused == 1
     assert da.decode_attn_plan(da.make_shape(tiles=dict(step_mode=2), **pages)).fused == 0
+
+
+def _table_rows():
+    rows = []
+    with open(os.path.join(ROOT, "decode_attention_output_amd", "csrc", "tile_table.inc")) as f:
+        for line in f:
+            if line.startswith("TILE_ENTRY("):
+                rows.append([int(v) for v in line[len("TILE_ENTRY("):line.index(")")].split(",")])
+    return rows
+
+
+def test_measured_tile_table_rows_are_valid_and_used(lib):
+    fields = ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit", "step_mode")
+    for row in _table_rows():
+        shape = dict(batch=row[0], num_q_heads=row[1], num_kv_heads=row[2], max_seq_len=row[3], hidden=row[4])
+        tiles = dict(zip(fields, row[5:]))
+        assert da.decode_attn_workspace_size(da.make_shape(**shape)) > 0, row
+        # a call without an override plans exactly as one that passes the row's tiles
+        a = da.decode_attn_plan(da.make_shape(**shape))
+        b = da.decode_attn_plan(da.make_shape(tiles=tiles, **shape))
+        for name in ("qk", "pv", "oproj"):
+            assert getattr(a, name).as_dict() == getattr(b, name).as_dict(), (row, name)
+        assert (a.fused, a.split_len, a.workspace_bytes) == (b.fused, b.split_len, b.workspace_bytes)
