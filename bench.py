@@ -101,7 +101,7 @@ def summarize_profile(args):
     wl = workloads.BY_NAME[args.workload]
     s = wl.shape
     seq_lens = workloads.draw_seq_lens(wl, np.random.default_rng(wl.seed))
-    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden))
+    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden, s.head_dim))
     kname, kbytes, _ = dominant_kernel(wl, plan, seq_lens)
 
     def counter_avg(path, counter, match):
@@ -233,7 +233,7 @@ def main():
         st["step"] = da.DecodeStep(st["q"], st["k"], st["v"], sl, st["o_weight"], out=st["out"], workspace=st["ws"],
                                    stream=stream)
 
-    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden))
+    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden, s.head_dim))
 
     # ---- warm-up, then exactly `steps` timed steps (one prepared C-ABI call each) ----
     for i in range(args.warmup):

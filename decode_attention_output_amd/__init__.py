@@ -26,6 +26,7 @@ DA_ERR_ALIGN = -3
 DA_ERR_WORKSPACE = -4
 DA_ERR_LAUNCH = -5
 DA_HEAD_DIM = 128
+DA_HEAD_DIM_WIDE = 256
 DA_MAX_GROUP = 16
 DA_FLAG_DEBUG_SCORES = 1
 DA_FLAG_SEPARATE = 2

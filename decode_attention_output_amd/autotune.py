@@ -66,14 +66,16 @@ TILE_FIELDS = ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit", "s
 
 def emit_entry(path, shape, tiles, note):
     """Insert or replace the table row of `shape` (a dict of batch, num_q_heads, num_kv_heads,
-    max_seq_len, hidden); the header comment and the other rows are kept, rows sorted by shape."""
-    key = (shape["batch"], shape["num_q_heads"], shape["num_kv_heads"], shape["max_seq_len"], shape["hidden"])
+    head_dim, max_seq_len, hidden); the header comment and the other rows are kept, rows sorted
+    by shape."""
+    key = (shape["batch"], shape["num_q_heads"], shape["num_kv_heads"], shape["head_dim"], shape["max_seq_len"],
+           shape["hidden"])
     head, rows = [], {}
     with open(path) as f:
         for line in f:
             if line.startswith("TILE_ENTRY("):
                 vals = [int(v) for v in line[len("TILE_ENTRY("):line.index(")")].split(",")]
-                rows[tuple(vals[:5])] = line
+                rows[tuple(vals[:6])] = line
             else:
                 head.append(line)
     vals = list(key) + [int(tiles.get(n, 0)) for n in TILE_FIELDS]
@@ -198,7 +200,7 @@ def main(argv=None):
                 best_proj, best_proj_us = t, us
 
     best, best_us = best_proj, best_proj_us
-    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden))
+    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden, s.head_dim))
     if "mode" not in skip and plan.fused:
         # the single-launch step: attention workgroups aimed at x projection column tile
         for w, tn in itertools.product([0] + _parse_list(args.step_wgs), [0, 128, 256, 512]):
@@ -208,7 +210,7 @@ def main(argv=None):
                 best, best_us = t, us
     builtin_us = try_tiles("builtin", {}, step_calls, ref_out, "out", alg_bytes)
     shape = {"batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
-             "max_seq_len": s.max_seq_len, "hidden": s.hidden}
+             "max_seq_len": s.max_seq_len, "hidden": s.hidden, "head_dim": s.head_dim}
     print(json.dumps({"workload": wl.name, "best": best, "best_us": round(best_us, 3),
                       "builtin_us": None if builtin_us is None else round(builtin_us, 3), "shape": shape}),
           flush=True)

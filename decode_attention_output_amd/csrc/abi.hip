@@ -45,14 +45,14 @@ bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
 
 // ---- the measured tile table (tile_table.inc, written by autotune.py) ----
 struct TileEntry {
-  int32_t B, Hq, Hkv, Lmax, N;
+  int32_t B, Hq, Hkv, D, Lmax, N;
   decode_attn_tiles_t tiles;
 };
 constexpr TileEntry kTileTable[] = {
-#define TILE_ENTRY(b, hq, hkv, lmax, n, w, d, tn, ks, mode) {b, hq, hkv, lmax, n, {w, d, tn, ks, mode}},
+#define TILE_ENTRY(b, hq, hkv, d, lmax, n, w, dp, tn, ks, mode) {b, hq, hkv, d, lmax, n, {w, dp, tn, ks, mode}},
 #include "tile_table.inc"
 #undef TILE_ENTRY
-    {0, 0, 0, 0, 0, {0, 0, 0, 0, 0}},  // end of the table
+    {0, 0, 0, 0, 0, 0, {0, 0, 0, 0, 0}},  // end of the table
 };
 
 // The shape a call runs with: the caller's, plus the table's tiles for its
@@ -61,8 +61,8 @@ decode_attn_shape_t effective_shape(const decode_attn_shape_t* s) {
   decode_attn_shape_t e = *s;
   if (e.tiles) return e;
   for (const TileEntry& t : kTileTable)
-    if (t.B == e.batch && t.Hq == e.num_q_heads && t.Hkv == e.num_kv_heads && t.Lmax == e.max_seq_len &&
-        t.N == e.hidden && t.B > 0) {
+    if (t.B == e.batch && t.Hq == e.num_q_heads && t.Hkv == e.num_kv_heads && t.D == e.head_dim &&
+        t.Lmax == e.max_seq_len && t.N == e.hidden && t.B > 0) {
       e.tiles = &t.tiles;
       break;
     }
@@ -86,14 +86,15 @@ bool tiles_ok(const decode_attn_shape_t* s) {
 
 bool shape_ok(const decode_attn_shape_t* s, bool need_hidden) {
   if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->max_seq_len < 1) return false;
-  if (s->head_dim != kHeadDim) return false;
+  if (s->head_dim != 128 && s->head_dim != 256) return false;
+  if (s->head_dim != 128 && s->tiles && s->tiles->attn_depth > 1) return false;
   if (s->num_q_heads % s->num_kv_heads != 0) return false;
   if (s->num_q_heads / s->num_kv_heads > DA_MAX_GROUP) return false;
   if (need_hidden && (s->hidden < 1 || s->hidden % 8 != 0)) return false;
   if (s->batch > da::kMaxAttnBatch) return false;
-  if (s->max_seq_len > (1 << 24)) return false;  // one sequence's K rows stay below 4 GiB
+  if ((size_t)s->max_seq_len * s->head_dim * 2 >= (1ull << 32)) return false;  // one sequence's K rows < 4 GiB
   // element counts must stay addressable
-  const double kv = (double)s->batch * s->num_kv_heads * s->max_seq_len * kHeadDim;
+  const double kv = (double)s->batch * s->num_kv_heads * s->max_seq_len * s->head_dim;
   if (kv > 9.0e15) return false;
   return tiles_ok(s);
 }
@@ -187,7 +188,7 @@ AttnPlan plan_attn(const decode_attn_shape_t* s) {
   }
   ap.keys_per_wg = ceil_div(blocks_max, ap.workgroups) * kAttnBlockKeys;
   ap.slots = (size_t)ap.workgroups + (size_t)pairs;
-  ap.part_o_bytes = align_up(ap.slots * G * kHeadDim * sizeof(float), kAlign);
+  ap.part_o_bytes = align_up(ap.slots * G * s->head_dim * sizeof(float), kAlign);
   ap.part_ml_bytes = align_up(ap.slots * G * 2 * sizeof(float), kAlign);
   return ap;
 }
@@ -222,7 +223,8 @@ StepPlan plan_step(const decode_attn_shape_t* s) {
   StepPlan sp{};
   const int B = s->batch, Hkv = s->num_kv_heads, G = s->num_q_heads / s->num_kv_heads;
   const int K = s->num_q_heads * kHeadDim, N = s->hidden;
-  if (B > kStepMaxBatch || (s->flags & DA_FLAG_DEBUG_SCORES)) return sp;
+  // (head_dim 128 only: the step's projection works in whole 128-dim query heads)
+  if (B > kStepMaxBatch || (s->flags & DA_FLAG_DEBUG_SCORES) || s->head_dim != kHeadDim) return sp;
   if ((size_t)B * Hkv * s->max_seq_len * kHeadDim * 4 > kStepMaxKvBytes) return sp;
   if ((size_t)K * N * 2 > kStepMaxWeightBytes) return sp;
   sp.gpad = pow2_at_least(G);
@@ -292,10 +294,10 @@ Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
   L.fused = false;
   if (with_proj) {
     const decode_attn_tiles_t* t = s->tiles;
-    L.proj = plan_proj(s->batch, s->num_q_heads * kHeadDim, s->hidden, t ? t->proj_tile_n : 0,
+    L.proj = plan_proj(s->batch, s->num_q_heads * s->head_dim, s->hidden, t ? t->proj_tile_n : 0,
                        t ? t->proj_ksplit : 0);
     L.off_flat = off;
-    off += align_up((size_t)s->batch * s->num_q_heads * kHeadDim * sizeof(uint16_t), kAlign);
+    off += align_up((size_t)s->batch * s->num_q_heads * s->head_dim * sizeof(uint16_t), kAlign);
     L.off_proj_part = off;
     off += L.proj.part_bytes;
     L.proj_counter0 = counters;
@@ -357,9 +359,10 @@ da::AttnParams attn_params(const void* q, const void* k, const void* v, const in
   p.Hkv = s->num_kv_heads;
   p.G = s->num_q_heads / s->num_kv_heads;
   p.Lmax = s->max_seq_len;
+  p.head_dim = s->head_dim;
   p.num_workgroups = L.attn.workgroups;
   p.step_variant = L.attn.depth;
-  const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
+  const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)s->head_dim);
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   return p;
@@ -472,7 +475,8 @@ int decode_attn_plan(const decode_attn_shape_t* shape_in, decode_attn_plan_t* pl
   const Layout L = layout_for(shape, true);
   if (!L.fits) return DA_ERR_SHAPE;
   const int G = shape->num_q_heads / shape->num_kv_heads;
-  const int Ko = shape->num_q_heads * kHeadDim;
+  const int D = shape->head_dim;
+  const int Ko = shape->num_q_heads * D;
   memset(plan, 0, sizeof *plan);
   if (L.fused) {
     // one launch: a fixed number of pieces per sequence, projection tiles of whole kv heads
@@ -490,9 +494,9 @@ int decode_attn_plan(const decode_attn_shape_t* shape_in, decode_attn_plan_t* pl
   }
   const int wgs = L.attn.workgroups;
   // QK^T per kv head: M = G, K = head_dim (whole), N = keys (32 per wave step)
-  plan->qk = {G, kHeadDim, shape->max_seq_len, 16, kHeadDim, kAttnBlockKeys, wgs, wgs};
+  plan->qk = {G, D, shape->max_seq_len, 16, D, kAttnBlockKeys, wgs, wgs};
   // attn x V per kv head: M = G, K = keys (32 per wave step), N = head_dim (whole)
-  plan->pv = {G, shape->max_seq_len, kHeadDim, 16, kAttnBlockKeys, kHeadDim, wgs, wgs};
+  plan->pv = {G, shape->max_seq_len, D, 16, kAttnBlockKeys, D, wgs, wgs};
   plan->oproj = {shape->batch, Ko, shape->hidden, L.proj.mpad, L.proj.kchunk, L.proj.tile_n, L.proj.ksplit,
                  L.proj.tiles * L.proj.ksplit};
   plan->split_len = L.attn.keys_per_wg;
@@ -523,7 +527,7 @@ int decode_attn_fwd(const void* q, const void* k_cache, const void* v_cache, con
   const da::AttnParams p = attn_params(q, k_cache, v_cache, seq_lens, flat, shape, L);
   if (L.fused) return run_step(q, k_cache, v_cache, seq_lens, o_weight, out, shape, L, st);
   if ((rc = run_attention(p, L, st))) return rc;
-  return run_proj(L.proj, flat, o_weight, out, shape->batch, shape->num_q_heads * kHeadDim, shape->hidden,
+  return run_proj(L.proj, flat, o_weight, out, shape->batch, shape->num_q_heads * shape->head_dim, shape->hidden,
                   ws + L.off_proj_part, (char*)((uint32_t*)ws + L.proj_counter0), st);
 }
 

@@ -9,29 +9,35 @@ namespace da {
 
 namespace {
 
-template <int GP, int NW, int D>
-__global__ __launch_bounds__(NW* kWave, D == 1 ? 2 : 1) void attn_streamk_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[attn_streamk_lds<NW>()];
-  attn_streamk_body<GP, NW, D>(p, blockIdx.x, gridDim.x, smem);
+// head_dim 128: two workgroups fit a compute unit at one step in flight per
+// wave; deeper pipelines and head_dim 256 (whose K/V tile per step is twice
+// as large) use one workgroup per compute unit and its AGPRs.
+template <int GP, int NW, int D, int HD>
+__global__ __launch_bounds__(NW* kWave, (D == 1 && HD == 128) ? 2 : 1) void attn_streamk_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[attn_streamk_lds<NW, HD>()];
+  attn_streamk_body<GP, NW, D, HD>(p, blockIdx.x, gridDim.x, smem);
 }
 
 }  // namespace
 
-template <int GP, int D>
+template <int GP, int D, int HD>
 static hipError_t launch_variant(const AttnParams& p, hipStream_t s) {
-  attn_streamk_kernel<GP, kAttnWaves, D><<<dim3(p.num_workgroups), dim3(kAttnWaves * kWave), 0, s>>>(p);
+  attn_streamk_kernel<GP, kAttnWaves, D, HD><<<dim3(p.num_workgroups), dim3(kAttnWaves * kWave), 0, s>>>(p);
   return hipGetLastError();
 }
 
 // Pipeline depth (32-key steps in flight per wave while one is computed): 1 by
-// default (the registers of a step drain to LDS as it begins), 2..3 selectable.
+// default (the registers of a step drain to LDS as it begins), 2..3 selectable
+// at head_dim 128; head_dim 256 runs one step in flight.
 template <int GP>
 static hipError_t launch_gp(const AttnParams& p, hipStream_t s) {
+  if (p.head_dim == 256) return p.step_variant <= 1 ? launch_variant<GP, 1, 256>(p, s) : hipErrorInvalidValue;
+  if (p.head_dim != 128) return hipErrorInvalidValue;
   switch (p.step_variant) {
-    case 0: return launch_variant<GP, 1>(p, s);
-    case 1: return launch_variant<GP, 1>(p, s);
-    case 2: return launch_variant<GP, 2>(p, s);
-    case 3: return launch_variant<GP, 3>(p, s);
+    case 0: return launch_variant<GP, 1, 128>(p, s);
+    case 1: return launch_variant<GP, 1, 128>(p, s);
+    case 2: return launch_variant<GP, 2, 128>(p, s);
+    case 3: return launch_variant<GP, 3, 128>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

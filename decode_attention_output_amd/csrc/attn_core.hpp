@@ -71,32 +71,52 @@ __device__ __forceinline__ void rsrc_st8_coherent(rsrc_t r, uint32_t off, uint2 
 
 // ---- per-wave running state ----
 // The wave's 16 MFMA columns are query rows (G valid, the rest zero queries).
-struct AttnWave {
-  float m_ref;   // reference max of query lane%16 (log2 units), equal in the 4 lane groups
-  float l_acc;   // sum of this lane's weights of query lane%16
-  f32x4_t o[8];  // O[query 4g + r][dim 16j + lane%16] in element r of o[j]
+template <int HD>
+struct AttnWaveT {
+  float m_ref;        // reference max of query lane%16 (log2 units), equal in the 4 lane groups
+  float l_acc;        // sum of this lane's weights of query lane%16
+  f32x4_t o[HD / 16]; // O[query 4g + r][dim 16j + lane%16] in element r of o[j]
 
   __device__ __forceinline__ void reset() {
     m_ref = -INFINITY;
     l_acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < HD / 16; ++j) o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 };
+using AttnWave = AttnWaveT<kHeadDim>;
 
-constexpr int kStepKeys = 32;                     // keys per wave step
-constexpr int kStageRow = kRowBytes + 16;         // padded LDS row: consecutive rows 4 banks apart
-constexpr int kStageTile = kStepKeys * kStageRow; // one 32-key K or V tile
-constexpr int kStageBytes = 2 * kStageTile;       // LDS of one wave: K tile, V tile
+constexpr int kStepKeys = 32;  // keys per wave step
 
-// One step's K and V as loaded: element c holds row 4c + lane/16, bytes (lane%16)*16.
-struct KVTile {
-  uint4 k[8], v[8];
+// Sizes of one head_dim HD (128 or 256): a K or V row is 2*HD bytes; one load
+// instruction of a wave reads 1 KiB, i.e. kRowsPerLoad whole rows, and a lane
+// holds kLoads 16-byte pieces of a 32-key K (or V) tile: piece c is row
+// kRowsPerLoad*c + lane/kLanesPerRow, bytes (lane%kLanesPerRow)*16. In LDS
+// every row is padded by 16 bytes (consecutive rows 4 banks apart).
+template <int HD>
+struct Dims {
+  static constexpr int kRowBytes = HD * 2;
+  static constexpr int kLanesPerRow = kRowBytes / 16;
+  static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
+  static constexpr int kLoads = kStepKeys / kRowsPerLoad;
+  static constexpr int kStageRow = kRowBytes + 16;
+  static constexpr int kStageTile = kStepKeys * kStageRow;  // one 32-key K or V tile
+  static constexpr int kStageBytes = 2 * kStageTile;        // LDS of one wave: K tile, V tile
 };
+constexpr int kStageRow = Dims<kHeadDim>::kStageRow;
+constexpr int kStageTile = Dims<kHeadDim>::kStageTile;
+constexpr int kStageBytes = Dims<kHeadDim>::kStageBytes;
+
+// One step's K and V as loaded (see Dims).
+template <int HD>
+struct KVTileT {
+  uint4 k[Dims<HD>::kLoads], v[Dims<HD>::kLoads];
+};
+using KVTile = KVTileT<kHeadDim>;
 
 // Everything a wave needs to know about the (batch, kv head) it works on.
 struct AttnSeg {
-  rsrc_t K, V;    // [L, 128] bf16 rows of this (batch, kv head); reads past L return 0
+  rsrc_t K, V;    // [L, head_dim] bf16 rows of this (batch, kv head); reads past L return 0
   int L;          // keys of the sequence
   int G;          // query heads of the group
   float scale_log2;
@@ -107,26 +127,32 @@ struct AttnSeg {
 
 // B operand of S^T = K x Q^T: lane (query col, group grp) holds dims
 // kk*32 + grp*8 .. +8 of its query (zero for col >= G).
-__device__ __forceinline__ void load_query(uint4 (&qa)[4], const uint16_t* q_rows, int G, int col, int grp) {
+template <int HD = kHeadDim>
+__device__ __forceinline__ void load_query(uint4 (&qa)[HD / 32], const uint16_t* q_rows, int G, int col, int grp) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    qa[kk] = (col < G) ? ld16(q_rows + (size_t)col * kHeadDim + kk * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
+  for (int kk = 0; kk < HD / 32; ++kk)
+    qa[kk] = (col < G) ? ld16(q_rows + (size_t)col * HD + kk * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
 }
 
-__device__ __forceinline__ void load_kv(KVTile& t, const AttnSeg& sg, int key0, int lane) {
-  const uint32_t off = (uint32_t)(key0 + (lane >> 4)) * kRowBytes + (lane & 15) * 16;
+template <int HD = kHeadDim>
+__device__ __forceinline__ void load_kv(KVTileT<HD>& t, const AttnSeg& sg, int key0, int lane) {
+  using Dm = Dims<HD>;
+  const uint32_t off = (uint32_t)(key0 + lane / Dm::kLanesPerRow) * Dm::kRowBytes + (lane % Dm::kLanesPerRow) * 16;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) t.k[c] = rsrc_ld16(sg.K, off + c * 4 * kRowBytes);
+  for (int c = 0; c < Dm::kLoads; ++c) t.k[c] = rsrc_ld16(sg.K, off + c * Dm::kRowsPerLoad * Dm::kRowBytes);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) t.v[c] = rsrc_ld16(sg.V, off + c * 4 * kRowBytes);
+  for (int c = 0; c < Dm::kLoads; ++c) t.v[c] = rsrc_ld16(sg.V, off + c * Dm::kRowsPerLoad * Dm::kRowBytes);
 }
 
-__device__ __forceinline__ void stage_kv(char* stage, const KVTile& t, int lane) {
-  char* p = stage + (lane >> 4) * kStageRow + (lane & 15) * 16;
+template <int HD = kHeadDim>
+__device__ __forceinline__ void stage_kv(char* stage, const KVTileT<HD>& t, int lane) {
+  using Dm = Dims<HD>;
+  char* p = stage + (lane / Dm::kLanesPerRow) * Dm::kStageRow + (lane % Dm::kLanesPerRow) * 16;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(p + c * 4 * kStageRow) = t.k[c];
+  for (int c = 0; c < Dm::kLoads; ++c) *reinterpret_cast<uint4*>(p + c * Dm::kRowsPerLoad * Dm::kStageRow) = t.k[c];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) *reinterpret_cast<uint4*>(p + kStageTile + c * 4 * kStageRow) = t.v[c];
+  for (int c = 0; c < Dm::kLoads; ++c)
+    *reinterpret_cast<uint4*>(p + Dm::kStageTile + c * Dm::kRowsPerLoad * Dm::kStageRow) = t.v[c];
 }
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -151,18 +177,20 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 
 // One 32-key step starting at key0, whose K/V tile is in the wave's stage;
 // keys >= end are masked out.
-template <int GP>
-__device__ __forceinline__ void attn_step(AttnWave& w, const char* stage, const uint4 (&qb)[4], const AttnSeg& sg,
-                                          int key0, int end, int lane) {
+template <int GP, int HD = kHeadDim>
+__device__ __forceinline__ void attn_step(AttnWaveT<HD>& w, const char* stage, const uint4 (&qb)[HD / 32],
+                                          const AttnSeg& sg, int key0, int end, int lane) {
+  using Dm = Dims<HD>;
   const int i = lane & 15, g = lane >> 4;
   // ---- S^T = K x Q^T, two 16-key tiles ----
   f32x4_t sc[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     sc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const char* kr = stage + (16 * tt + i) * kStageRow + g * 16;
+    const char* kr = stage + (16 * tt + i) * Dm::kStageRow + g * 16;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) sc[tt] = mfma_bf16(*reinterpret_cast<const uint4*>(kr + kk * 64), qb[kk], sc[tt]);
+    for (int kk = 0; kk < HD / 32; ++kk)
+      sc[tt] = mfma_bf16(*reinterpret_cast<const uint4*>(kr + kk * 64), qb[kk], sc[tt]);
   }
   // lane (i, g) holds the scores of query i for keys 16tt + 4g + r
   float s2[2][4];
@@ -198,7 +226,7 @@ __device__ __forceinline__ void attn_step(AttnWave& w, const char* stage, const 
 #pragma unroll
     for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < HD / 16; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) w.o[j][r] *= ar[r];
   }
@@ -230,44 +258,47 @@ __device__ __forceinline__ void attn_step(AttnWave& w, const char* stage, const 
   };
   const uint4 a_hi = pack(hi), a_mid = pack(mid), a_lo = pack(lo);
 
-  // ---- O += P x V, 16 dims per product ----
-  const char* vt = stage + kStageTile + (4 * g + (i >> 2)) * kStageRow + (i & 3) * 8;
-  uint4 vb[8];
+  // ---- O += P x V, 16 dims per product, 128 dims at a time ----
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint2 v0 = lds_read_tr16(vt + j * 32);
-    const uint2 v1 = lds_read_tr16(vt + 16 * kStageRow + j * 32);
-    vb[j] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+  for (int h0 = 0; h0 < HD / 16; h0 += 8) {
+    const char* vt = stage + Dm::kStageTile + (4 * g + (i >> 2)) * Dm::kStageRow + (i & 3) * 8 + h0 * 32;
+    uint4 vb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint2 v0 = lds_read_tr16(vt + j * 32);
+      const uint2 v1 = lds_read_tr16(vt + 16 * Dm::kStageRow + j * 32);
+      vb[j] = make_uint4(v0.x, v0.y, v1.x, v1.y);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w.o[h0 + j] = mfma_bf16(a_hi, vb[j], w.o[h0 + j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w.o[h0 + j] = mfma_bf16(a_mid, vb[j], w.o[h0 + j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w.o[h0 + j] = mfma_bf16(a_lo, vb[j], w.o[h0 + j]);
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w.o[j] = mfma_bf16(a_hi, vb[j], w.o[j]);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w.o[j] = mfma_bf16(a_mid, vb[j], w.o[j]);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w.o[j] = mfma_bf16(a_lo, vb[j], w.o[j]);
 }
 
 // The wave's steps first, first+step, ... (n of them, 32 keys each). D
 // register sets: a set is parked in LDS as its step begins and at once takes
 // the loads of the step D later, so D steps are in flight during a step.
-template <int GP, int D>
-__device__ __forceinline__ void attn_wave_steps(AttnWave& w, const uint4 (&qb)[4], const AttnSeg& sg, int first,
-                                                int step, int n, int end, char* stage, int lane) {
+template <int GP, int D, int HD = kHeadDim>
+__device__ __forceinline__ void attn_wave_steps(AttnWaveT<HD>& w, const uint4 (&qb)[HD / 32], const AttnSeg& sg,
+                                                int first, int step, int n, int end, char* stage, int lane) {
   if (n <= 0) return;
-  KVTile t[D];
+  KVTileT<HD> t[D];
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (j < n) load_kv(t[j], sg, (first + j * step) * kStepKeys, lane);
+    if (j < n) load_kv<HD>(t[j], sg, (first + j * step) * kStepKeys, lane);
   for (int i0 = 0; i0 < n; i0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int i = i0 + j;
       if (i < n) {
         wave_lds_fence();  // the previous step's LDS reads come first
-        stage_kv(stage, t[j], lane);
-        if (i + D < n) load_kv(t[j], sg, (first + (i + D) * step) * kStepKeys, lane);
+        stage_kv<HD>(stage, t[j], lane);
+        if (i + D < n) load_kv<HD>(t[j], sg, (first + (i + D) * step) * kStepKeys, lane);
         wave_lds_fence();
-        attn_step<GP>(w, stage, qb, sg, (first + i * step) * kStepKeys, end, lane);
+        attn_step<GP, HD>(w, stage, qb, sg, (first + i * step) * kStepKeys, end, lane);
       }
     }
   }
@@ -301,8 +332,8 @@ __device__ __forceinline__ void attn_wave_steps_preloaded(AttnWave& w, KVTile& t
 
 // Park the wave's state in LDS: so[g][128], sm[g], sl[g] for g < GP. These
 // may overlap the wave's own stage (its last reads are complete).
-template <int GP>
-__device__ __forceinline__ void attn_wave_to_lds(AttnWave& w, float (*so)[kHeadDim], float* sm, float* sl, int lane) {
+template <int GP, int HD = kHeadDim>
+__device__ __forceinline__ void attn_wave_to_lds(AttnWaveT<HD>& w, float (*so)[HD], float* sm, float* sl, int lane) {
   const int i = lane & 15, g = lane >> 4;
   float l = w.l_acc;
   l += __shfl_xor(l, 16);
@@ -313,7 +344,7 @@ __device__ __forceinline__ void attn_wave_to_lds(AttnWave& w, float (*so)[kHeadD
     const int q = 4 * g + r;
     if (q < GP) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) so[q][16 * j + i] = w.o[j][r];
+      for (int j = 0; j < HD / 16; ++j) so[q][16 * j + i] = w.o[j][r];
     }
   }
   if (g == 0 && i < GP) {

@@ -30,17 +30,20 @@ __device__ __forceinline__ long range_owner(long x, long T, long W) { return T >
 // same bytes later hold the waves' outputs and the merge scratch; each use is
 // separated from the next by a barrier).
 constexpr int kAttnTableBytes = ((2 * kMaxAttnBatch + 1) * 4 + 15) / 16 * 16;
-template <int NW>
+template <int NW, int HD>
 constexpr int attn_streamk_lds() {
-  return kAttnTableBytes + NW * kStageBytes;
+  return kAttnTableBytes + NW * Dims<HD>::kStageBytes;
 }
 
-// One workgroup's share of the stream-K attention: workgroup `wg` of `W`;
-// `smem` is attn_streamk_lds<NW>() bytes of LDS, 16-byte aligned.
-template <int GP, int NW, int D>
+// One workgroup's share of the stream-K attention: workgroup `wg` of `W`,
+// head_dim HD; `smem` is attn_streamk_lds<NW, HD>() bytes of LDS, 16-byte aligned.
+template <int GP, int NW, int D, int HD>
 __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, long W, char* smem) {
   constexpr int NT = NW * kWave;
-  constexpr int kWaveOut = GP * kHeadDim * 4;  // a wave's un-normalised output in its stage
+  constexpr int kStageBytes = Dims<HD>::kStageBytes;
+  constexpr int kRowBytes = Dims<HD>::kRowBytes;
+  constexpr int D4 = HD / 4;                // groups of 4 dims of one head
+  constexpr int kWaveOut = GP * HD * 4;     // a wave's un-normalised output in its stage
   static_assert(kWaveOut + 2 * GP * 4 <= kStageBytes, "a wave's output fits its stage");
   static_assert(NT * 24 <= kStageBytes && NT * 4 <= kStageBytes, "merge scratch fits one stage");
   int* const s_pre = reinterpret_cast<int*>(smem);  // blocks of the sequences before batch b (per kv head)
@@ -50,7 +53,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   float* const s_cm = reinterpret_cast<float*>(s_stage);
   float* const s_cl = s_cm + NT;
   float4* const s_co = reinterpret_cast<float4*>(s_cl + NT);
-  auto s_o = [&](int w) { return reinterpret_cast<float (*)[kHeadDim]>(s_stage + w * kStageBytes); };
+  auto s_o = [&](int w) { return reinterpret_cast<float (*)[HD]>(s_stage + w * kStageBytes); };
   auto s_m = [&](int w) { return reinterpret_cast<float*>(s_stage + w * kStageBytes + kWaveOut); };
   auto s_l = [&](int w) { return reinterpret_cast<float*>(s_stage + w * kStageBytes + kWaveOut + GP * 4); };
 
@@ -105,7 +108,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   auto store4 = [&](int b, int qh, int d4, const float (&o)[4], float inv) {
     const uint32_t w01 = (uint32_t)f32_to_bf16_rne(o[0] * inv) | ((uint32_t)f32_to_bf16_rne(o[1] * inv) << 16);
     const uint32_t w23 = (uint32_t)f32_to_bf16_rne(o[2] * inv) | ((uint32_t)f32_to_bf16_rne(o[3] * inv) << 16);
-    *reinterpret_cast<uint2*>(p.flat + ((size_t)b * p.Hq + qh) * kHeadDim + d4 * 4) = make_uint2(w01, w23);
+    *reinterpret_cast<uint2*>(p.flat + ((size_t)b * p.Hq + qh) * HD + d4 * 4) = make_uint2(w01, w23);
   };
 
   // ---- the piece that starts at block y: its sequence (b, h) and block range ----
@@ -139,7 +142,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   };
   auto seg_of = [&](const Piece& pc) {
     AttnSeg sg;
-    const size_t kv_off = (size_t)pc.seg * p.Lmax * kHeadDim;
+    const size_t kv_off = (size_t)pc.seg * p.Lmax * HD;
     sg.K = make_rsrc(p.k + kv_off, (uint32_t)pc.L * kRowBytes);
     sg.V = make_rsrc(p.v + kv_off, (uint32_t)pc.L * kRowBytes);
     sg.L = pc.L;
@@ -150,8 +153,8 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
     sg.dbg_stride = p.Lmax;
     return sg;
   };
-  auto query_of = [&](uint4 (&qa)[4], const Piece& pc) {
-    load_query(qa, p.q + ((size_t)pc.b * p.Hq + (size_t)pc.h * G) * kHeadDim, G, col, grp);
+  auto query_of = [&](uint4 (&qa)[HD / 32], const Piece& pc) {
+    load_query<HD>(qa, p.q + ((size_t)pc.b * p.Hq + (size_t)pc.h * G) * HD, G, col, grp);
   };
   // this wave's 32-key steps of a piece: the piece's keys [lb0*32, min(lb1*32, L)),
   // interleaved over the waves; every step holds at least one key of the sequence
@@ -161,14 +164,14 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   };
 
   // ---- the end of a piece: merge the waves, then write the sequence's output or store a partial ----
-  auto finish_piece = [&](const Piece& pc, AttnWave& aw) {
+  auto finish_piece = [&](const Piece& pc, AttnWaveT<HD>& aw) {
     const int b = pc.b, h = pc.h, seg = pc.seg;
-    attn_wave_to_lds<GP>(aw, s_o(wave), s_m(wave), s_l(wave), lane);
+    attn_wave_to_lds<GP, HD>(aw, s_o(wave), s_m(wave), s_l(wave), lane);
     __syncthreads();
     DA_TRACE(2);
     const int slot = seg + (int)wg;
-    for (int idx = t; idx < G * 32; idx += NT) {
-      const int g = idx >> 5, d4 = idx & 31;
+    for (int idx = t; idx < G * D4; idx += NT) {
+      const int g = idx / D4, d4 = idx % D4;
       float M = s_m(0)[g];
 #pragma unroll
       for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m(w)[g]);
@@ -188,7 +191,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
         store4(b, qh, d4, O, 1.f / Ls);
         if (p.dbg_lse && d4 == 0) p.dbg_lse[(size_t)b * p.Hq + qh] = (M + log2f(Ls)) * kLn2;
       } else {
-        const uint32_t so = ((uint32_t)(slot * G + g) * kHeadDim + d4 * 4) * 4;
+        const uint32_t so = ((uint32_t)(slot * G + g) * HD + d4 * 4) * 4;
         rsrc_st16_coherent(part_o, so, make_uint4(__builtin_bit_cast(uint32_t, O[0]), __builtin_bit_cast(uint32_t, O[1]),
                                                   __builtin_bit_cast(uint32_t, O[2]), __builtin_bit_cast(uint32_t, O[3])));
         if (d4 == 0)
@@ -207,14 +210,14 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
       if (last_piece) {
         // ---- the last piece merges the P partials at slots seg+first .. seg+last ----
         const int slot0 = seg + (int)first;
-        const int npairs = G * 32;
+        const int npairs = G * D4;
         for (int base = 0; base < npairs; base += NT) {
           const int cnt = min(npairs - base, NT);
           const int nph = NT / cnt;
           const int pr = base + t % cnt, ph = t / cnt;
           float M = -INFINITY, Ls = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
           if (ph < nph) {
-            const int g = pr >> 5, d4 = pr & 31;
+            const int g = pr / D4, d4 = pr % D4;
             for (int j0 = ph; j0 < P; j0 += kMergeBatch * nph) {
               uint2 ml[kMergeBatch];
               uint4 ov[kMergeBatch];
@@ -223,7 +226,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
                 const int j = j0 + u * nph;
                 const uint32_t sl = (uint32_t)((slot0 + min(j, P - 1)) * G + g);
                 ml[u] = rsrc_ld8_coherent(part_ml, sl * 8);
-                ov[u] = rsrc_ld16_coherent(part_o, (sl * kHeadDim + d4 * 4) * 4);
+                ov[u] = rsrc_ld16_coherent(part_o, (sl * HD + d4 * 4) * 4);
               }
 #pragma unroll
               for (int u = 0; u < kMergeBatch; ++u) {
@@ -246,7 +249,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
               const float o[4] = {o4.x, o4.y, o4.z, o4.w};
               merge_partial(Mf, Lf, Of, s_cm[t + q2 * cnt], s_cl[t + q2 * cnt], o);
             }
-            const int g = pr >> 5, d4 = pr & 31;
+            const int g = pr / D4, d4 = pr % D4;
             const int qh = h * G + g;
             store4(b, qh, d4, Of, 1.f / Lf);
             if (p.dbg_lse && d4 == 0) p.dbg_lse[(size_t)b * p.Hq + qh] = (Mf + log2f(Lf)) * kLn2;
@@ -262,11 +265,12 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   while (x < xe) {
     const Piece pc = piece_at(x);
     const AttnSeg sg = seg_of(pc);
-    uint4 qa[4];
+    uint4 qa[HD / 32];
     query_of(qa, pc);
-    AttnWave aw;
+    AttnWaveT<HD> aw;
     aw.reset();
-    attn_wave_steps<GP, D>(aw, qa, sg, pc.lb0 + wave, NW, wave_steps(pc), pc.L, s_stage + wave * kStageBytes, lane);
+    attn_wave_steps<GP, D, HD>(aw, qa, sg, pc.lb0 + wave, NW, wave_steps(pc), pc.L, s_stage + wave * kStageBytes,
+                               lane);
     finish_piece(pc, aw);
     x = pc.pe;
   }

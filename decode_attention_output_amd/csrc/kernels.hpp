@@ -23,20 +23,21 @@ constexpr int kAttnWaves = 4;        // wavefronts per stream-K attention workgr
 
 // Stream-K attention over all (batch, kv head) sequences of one step.
 struct AttnParams {
-  const uint16_t* q;        // bf16 [B, Hq, 128]
-  const uint16_t* k;        // bf16 [B, Hkv, Lmax, 128]
-  const uint16_t* v;        // bf16 [B, Hkv, Lmax, 128]
+  const uint16_t* q;        // bf16 [B, Hq, D]
+  const uint16_t* k;        // bf16 [B, Hkv, Lmax, D]
+  const uint16_t* v;        // bf16 [B, Hkv, Lmax, D]
   const int32_t* seq_lens;  // [B]
-  uint16_t* flat;           // bf16 [B, Hq*128] head-major attention output
-  float* part_o;            // fp32 [slots, G, 128] un-normalised partial outputs
+  uint16_t* flat;           // bf16 [B, Hq*D] head-major attention output
+  float* part_o;            // fp32 [slots, G, D] un-normalised partial outputs
   float* part_ml;           // fp32 [slots, G, 2]   (max in log2 units, weight sum)
   uint32_t part_o_bytes, part_ml_bytes;
   uint32_t* counters;       // [B * Hkv] arrival counters, zero between calls
   float* dbg_scores;        // optional fp32 [B, Hq, Lmax]
   float* dbg_lse;           // optional fp32 [B, Hq]
   int B, Hq, Hkv, G, Lmax;
+  int head_dim;             // 128 or 256
   int num_workgroups;       // stream-K workgroups; slots = num_workgroups + B * Hkv
-  int step_variant;         // 32-key steps in flight per wave: 0 = default (2), else 1..3
+  int step_variant;         // 32-key steps in flight per wave: 0 = default (1), else 1..3
   float scale;       // softmax scale (natural units)
   float scale_log2;  // scale * log2(e)
 };

@@ -47,8 +47,10 @@ extern "C" {
 #define DA_ERR_WORKSPACE (-4) /* workspace missing or smaller than required          */
 #define DA_ERR_LAUNCH (-5)    /* a kernel launch failed (hipGetLastError after it)   */
 
-/* Only head_dim 128 is implemented. */
+/* head_dim: 128 (every path) or DA_HEAD_DIM_WIDE (stream-K attention and the
+ * separate projection; the single-launch step is built for 128 only). */
 #define DA_HEAD_DIM 128
+#define DA_HEAD_DIM_WIDE 256
 /* Largest query-head group (num_q_heads / num_kv_heads). */
 #define DA_MAX_GROUP 16
 
@@ -68,7 +70,7 @@ extern "C" {
  *                   the single-launch step, the attention workgroups aimed at
  *                   (every sequence is cut into the same number of pieces)
  *  attn_depth       32-key steps each attention wave has in flight while it
- *                   computes one, 1..3
+ *                   computes one, 1..3 (1 only at head_dim 256)
  *  proj_tile_n      output columns per projection workgroup: 64, 128, 256 or
  *                   512 (the GEMV for B < 16 also needs tile_n * B <= 2048 after
  *                   B is rounded up to a power of two; the MFMA GEMM for
@@ -94,7 +96,7 @@ typedef struct {
  *  batch          B >= 1
  *  num_q_heads    Hq >= 1, a multiple of num_kv_heads, Hq/Hkv <= DA_MAX_GROUP
  *  num_kv_heads   Hkv >= 1
- *  head_dim       D, must be DA_HEAD_DIM
+ *  head_dim       D: DA_HEAD_DIM (128) or DA_HEAD_DIM_WIDE (256)
  *  max_seq_len    Lmax >= 1: rows per (batch, kv head) in the K/V caches
  *  hidden         N >= 1, output features of the projection (its K is Hq*D);
  *                 unused by decode_attn_only

@@ -64,7 +64,8 @@ def test_null_pointers_are_rejected(lib, which):
     assert lib.decode_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == da.DA_ERR_NULL
 
 
-@pytest.mark.parametrize("kw", [dict(head_dim=64), dict(num_q_heads=30), dict(num_q_heads=8 * 17),
+@pytest.mark.parametrize("kw", [dict(head_dim=64), dict(head_dim=192), dict(head_dim=512),
+                                dict(head_dim=256, tiles=dict(attn_depth=2)), dict(num_q_heads=30), dict(num_q_heads=8 * 17),
                                 dict(batch=0), dict(max_seq_len=0), dict(hidden=0), dict(hidden=4100),
                                 dict(num_kv_heads=0)])
 def test_bad_shapes_are_rejected(lib, kw):
@@ -236,8 +237,9 @@ def _table_rows():
 def test_measured_tile_table_rows_are_valid_and_used(lib):
     fields = ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit", "step_mode")
     for row in _table_rows():
-        shape = dict(batch=row[0], num_q_heads=row[1], num_kv_heads=row[2], max_seq_len=row[3], hidden=row[4])
-        tiles = dict(zip(fields, row[5:]))
+        shape = dict(batch=row[0], num_q_heads=row[1], num_kv_heads=row[2], head_dim=row[3], max_seq_len=row[4],
+                     hidden=row[5])
+        tiles = dict(zip(fields, row[6:]))
         assert da.decode_attn_workspace_size(da.make_shape(**shape)) > 0, row
         # a call without an override plans exactly as one that passes the row's tiles
         a = da.decode_attn_plan(da.make_shape(**shape))
@@ -245,3 +247,17 @@ def test_measured_tile_table_rows_are_valid_and_used(lib):
         for name in ("qk", "pv", "oproj"):
             assert getattr(a, name).as_dict() == getattr(b, name).as_dict(), (row, name)
         assert (a.fused, a.split_len, a.workspace_bytes) == (b.fused, b.split_len, b.workspace_bytes)
+
+
+def test_head_dim_256_plans_two_launches(lib):
+    # head_dim 256 runs the stream-K attention (QK^T with K = 256, attn x V with N = 256) and the
+    # separate projection with K = Hq * 256; the single-launch step is built for 128 only
+    cfg = dict(batch=1, num_q_heads=16, num_kv_heads=2, max_seq_len=2048, hidden=4096)
+    plan = da.decode_attn_plan(da.make_shape(head_dim=256, **cfg))
+    assert plan.fused == 0
+    assert (plan.qk.m, plan.qk.k, plan.qk.n) == (8, 256, 2048) and plan.qk.tile_k == 256
+    assert (plan.pv.m, plan.pv.k, plan.pv.n) == (8, 2048, 256) and plan.pv.tile_n == 256
+    assert (plan.oproj.m, plan.oproj.k, plan.oproj.n) == (1, 16 * 256, 4096)
+    # the attention partials and the bf16 attention output are twice as wide as at 128
+    narrow = da.decode_attn_workspace_size(da.make_shape(head_dim=128, flags=da.DA_FLAG_SEPARATE, **cfg))
+    assert plan.workspace_bytes > narrow

@@ -74,7 +74,7 @@ def test_decode_workload_small(gpu, wl):
     assert ref is not None
 
 
-@pytest.mark.parametrize("wl", [workloads.BATCHED, workloads.LONG], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [workloads.BATCHED, workloads.LONG, workloads.WIDE], ids=lambda w: w.name)
 def test_decode_workload_large(gpu, wl):
     inp = workloads.decode_inputs(wl, poison=True)
     res = _run_step(inp)
@@ -291,3 +291,38 @@ def test_tile_overrides_match_the_oracle(gpu, tiles, B):
     again = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, tiles=tiles))
     np.testing.assert_array_equal(out, again)
     _check_step(inp, {"flat": flat, "out": out}, what="tiles %s" % (tiles,))
+
+
+
+# ---- head_dim 256 (stream-K attention + separate projection) -------------
+
+WIDE = [
+    # (batch, Hq, Hkv, seq_lens, max_seq_len, hidden)
+    (1, 4, 1, [1], 1, 256),
+    (1, 8, 1, [33], 40, 512),
+    (2, 16, 2, [700, 5], 700, 1024),
+    (3, 8, 8, [129, 1, 2000], 2048, 264),
+    (1, 32, 2, [4096], 4096, 2048),   # group 16
+    (17, 4, 1, [64] * 17, 64, 256),   # the MFMA projection (17 rows)
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "B%d_H%d_KV%d_Lmax%d_N%d" % (c[0], c[1], c[2], c[4], c[5]))
+def test_head_dim_256_matches_the_oracle(gpu, case):
+    B, Hq, Hkv, sl, Lmax, hidden = case
+    inp = workloads.custom_decode_inputs(B, Hq, Hkv, sl, max_seq_len=Lmax, hidden=hidden, head_dim=256,
+                                         seed=400 + B * 10 + Hq)
+    res = _run_step(inp, debug=True)
+    _check_step(inp, res, what="head_dim 256 %s" % (case,))
+    att = oracle.attention(inp["q"], inp["k"], inp["v"], inp["seq_lens"], want_scores=True)
+    for b, L in enumerate(sl):
+        assert_scores_close(res["scores"][b, :, :L], att["scores"][b, :, :L], "head_dim 256 scores")
+    np.testing.assert_allclose(res["lse"], att["lse"], rtol=1e-5, atol=1e-5)
+
+
+def test_head_dim_256_single_key_is_bit_exact(gpu):
+    inp = workloads.custom_decode_inputs(2, 8, 2, [1, 1], max_seq_len=5, hidden=256, head_dim=256, seed=41)
+    res = _run_step(inp)
+    for b in range(2):
+        for qh in range(8):
+            np.testing.assert_array_equal(res["flat"][b, qh * 256:(qh + 1) * 256], inp["v"][b, qh // 4, 0])

@@ -69,9 +69,14 @@ BATCHED = DecodeWorkload("decode_b16_h32kv8_ragged1024-8192_o4096", DecodeShape(
 LONG = DecodeWorkload("decode_b4_h64kv8_L32768_o8192", DecodeShape(4, 64, 8, 128, 32768, 8192), seed=4,
                       seq_len=32768)
 
-ALL = [TINY, PAGES, GEMM, BATCHED, LONG]
+# head_dim 256 (not one of the five): a group of 8 query heads over 256-dim
+# keys, 16384 cached keys per sequence, 128 MiB of KV and a 32 MiB projection.
+WIDE = DecodeWorkload("decode_b4_h16kv2_d256_L16384_o4096", DecodeShape(4, 16, 2, 256, 16384, 4096), seed=5,
+                      seq_len=16384)
+
+ALL = [TINY, PAGES, GEMM, BATCHED, LONG, WIDE]
 BY_NAME = {w.name: w for w in ALL}
-DECODE = [TINY, PAGES, BATCHED, LONG]
+DECODE = [TINY, PAGES, BATCHED, LONG, WIDE]
 
 
 def _to_bf16_words(x: np.ndarray) -> np.ndarray:
