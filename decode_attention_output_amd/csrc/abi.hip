@@ -56,13 +56,15 @@ constexpr TileEntry kTileTable[] = {
 };
 
 // The shape a call runs with: the caller's, plus the table's tiles for its
-// exact shape when the caller brings no override.
-decode_attn_shape_t effective_shape(const decode_attn_shape_t* s) {
+// exact shape when the caller brings no override. An attention-only call has
+// no projection, so its hidden size is not compared (the row's attention
+// tiles apply).
+decode_attn_shape_t effective_shape(const decode_attn_shape_t* s, bool with_proj = true) {
   decode_attn_shape_t e = *s;
   if (e.tiles) return e;
   for (const TileEntry& t : kTileTable)
     if (t.B == e.batch && t.Hq == e.num_q_heads && t.Hkv == e.num_kv_heads && t.D == e.head_dim &&
-        t.Lmax == e.max_seq_len && t.N == e.hidden && t.B > 0) {
+        t.Lmax == e.max_seq_len && (!with_proj || t.N == e.hidden) && t.B > 0) {
       e.tiles = &t.tiles;
       break;
     }
@@ -464,7 +466,11 @@ size_t decode_attn_workspace_size(const decode_attn_shape_t* shape_in) {
   const decode_attn_shape_t* shape = &eff;
   if (!shape_ok(shape, true)) return 0;
   const Layout L = layout_for(shape, true);
-  return L.fits ? L.total : 0;
+  if (!L.fits) return 0;
+  // enough for decode_attn_only too, whose table lookup ignores the hidden size
+  const decode_attn_shape_t eff_attn = effective_shape(shape_in, false);
+  const Layout La = layout_for(&eff_attn, false);
+  return std::max(L.total, La.fits ? La.total : (size_t)0);
 }
 
 int decode_attn_plan(const decode_attn_shape_t* shape_in, decode_attn_plan_t* plan) {
@@ -534,7 +540,7 @@ int decode_attn_fwd(const void* q, const void* k_cache, const void* v_cache, con
 int decode_attn_only(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                      void* attn_out, const decode_attn_shape_t* shape_in, void* stream) {
   if (!shape_in) return DA_ERR_NULL;
-  const decode_attn_shape_t eff = effective_shape(shape_in);
+  const decode_attn_shape_t eff = effective_shape(shape_in, false);
   const decode_attn_shape_t* shape = &eff;
   int rc = check_attn_ptrs(q, k_cache, v_cache, seq_lens, attn_out);
   if (rc) return rc;
