@@ -1,0 +1,56 @@
+"""Host-side tools without a GPU: the tile-table writer of the measured tile
+search and the benchmark's command-line contract."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import decode_attention_output_amd as da
+from decode_attention_output_amd import autotune
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _rows(path):
+    with open(path) as f:
+        return [l for l in f if l.startswith("TILE_ENTRY(")]
+
+
+def test_emit_entry_inserts_replaces_and_sorts(tmp_path):
+    table = tmp_path / "tile_table.inc"
+    table.write_text(open(autotune.TABLE).read())
+    head = [l for l in open(autotune.TABLE) if not l.startswith("TILE_ENTRY(")]
+    big = dict(batch=64, num_q_heads=8, num_kv_heads=1, head_dim=128, max_seq_len=100, hidden=512)
+    small = dict(batch=2, num_q_heads=8, num_kv_heads=1, head_dim=256, max_seq_len=100, hidden=512)
+    n0 = len(_rows(table))
+    autotune.emit_entry(str(table), big, {"attn_workgroups": 96, "step_mode": 2}, "first")
+    autotune.emit_entry(str(table), small, {"proj_tile_n": 128}, "second")
+    autotune.emit_entry(str(table), big, {"attn_workgroups": 64}, "replaced")
+    rows = _rows(table)
+    assert len(rows) == n0 + 2
+    # the header comment is kept, rows are sorted by shape, a shape has one row
+    assert [l for l in open(table) if not l.startswith("TILE_ENTRY(")] == head
+    keys = [tuple(int(v) for v in r[len("TILE_ENTRY("):r.index(")")].split(",")[:6]) for r in rows]
+    assert keys == sorted(keys) and len(set(keys)) == len(keys)
+    mine = [r for r in rows if r.startswith("TILE_ENTRY(64, 8, 1, 128, 100, 512,")]
+    assert mine == ["TILE_ENTRY(64, 8, 1, 128, 100, 512, 64, 0, 0, 0, 0)  // replaced\n"]
+    assert "TILE_ENTRY(2, 8, 1, 256, 100, 512, 0, 0, 128, 0, 0)  // second\n" in rows
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_attention_only_workspace_covers_the_table_row():
+    # the head_dim 256 row of the table sets the stream-K grid; an attention-only call (whose
+    # hidden size is not part of the lookup) must fit the workspace the size query reports
+    shape = dict(batch=4, num_q_heads=16, num_kv_heads=2, max_seq_len=16384, head_dim=256)
+    rows = [r for r in _rows(autotune.TABLE) if r.startswith("TILE_ENTRY(4, 16, 2, 256, 16384,")]
+    assert rows, "the table holds the head_dim 256 workload's row"
+    w = int(rows[0][len("TILE_ENTRY("):].split(",")[6])
+    need_attn = da.decode_attn_workspace_size(da.make_shape(hidden=8, tiles=dict(attn_workgroups=w), **shape))
+    assert da.decode_attn_workspace_size(da.make_shape(hidden=8, **shape)) >= need_attn
