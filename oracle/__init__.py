@@ -18,6 +18,11 @@ What each function computes, and the pages it follows:
 * ``oproj`` -- the third matmul of that page, attn_output_flat x o_weight.
 * ``decode_step`` -- the three in sequence, the projection reading the bf16
   attention output.
+* ``prefill_attention`` -- context attention of a chunk of new tokens (the
+  same page names a context-attention kernel without defining it; the
+  plainest reading is taken: each token attends causally to the cached keys
+  up to its own position, with the decode step's softmax). T = 1 is exactly
+  ``attention``.
 * ``gemm_f16`` -- the BasicMatmul example of the CANN msKPP page
   "自动调优流程 / Kernel级自动调优": C = A x B, fp16, row-major.
 
@@ -78,6 +83,9 @@ def _load():
                                      _f64p, _u16p, _f64p, _f64p, _f64p, ci]
     lib.oracle_oproj.restype = ci
     lib.oracle_oproj.argtypes = [_u16p, _u16p, ci, ci, ci, _f64p, _u16p, ci]
+    lib.oracle_prefill_attention.restype = ci
+    lib.oracle_prefill_attention.argtypes = [_u16p, _u16p, _u16p, _i32p, ci, ci, ci, ci, ci, ci, ctypes.c_double,
+                                             _f64p, _u16p, ci]
     lib.oracle_gemm_f16.restype = ci
     lib.oracle_gemm_f16.argtypes = [_u16p, _u16p, ci, ci, ci, _f64p, _u16p, ci]
     lib.oracle_decode_step.restype = ci
@@ -173,6 +181,29 @@ def attention(q, k, v, seq_lens, scale=None, want_scores=False, nthreads=None):
     if want_scores:
         out.update(scores=scores, probs=probs, lse=lse)
     return out
+
+
+def prefill_attention(q, k, v, ctx_lens, scale=None, nthreads=None):
+    """Context attention of a chunk: q [B,T,Hq,D], k/v [B,Hkv,Lmax,D] (uint16 bf16 words), ctx_lens [B]
+    int32 (keys per sequence, the chunk's T tokens being the last T). Token t attends causally to keys
+    0 .. ctx_lens[b]-T+t. Returns a dict with ``out`` (uint16 [B,T,Hq*D]) and ``ref`` (float64, unrounded).
+    """
+    lib = _load()
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    cl = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    B, T, Hq, D = q.shape
+    Bk, Hkv, Lmax, Dk = k.shape
+    if Bk != B or Dk != D or v.shape != k.shape or cl.shape != (B,):
+        raise OracleError("prefill_attention: inconsistent shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    ref = np.empty((B, T, Hq * D), dtype=np.float64)
+    out = np.empty((B, T, Hq * D), dtype=np.uint16)
+    rc = lib.oracle_prefill_attention(_ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p), _ptr(cl, _i32p), B, T, Hq,
+                                      Hkv, D, Lmax, float(scale), _ptr(ref, _f64p), _ptr(out, _u16p),
+                                      nthreads or default_threads())
+    _check(rc, "prefill_attention")
+    return {"out": out, "ref": ref}
 
 
 def oproj(x, w, nthreads=None):

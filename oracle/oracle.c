@@ -292,6 +292,91 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
 }
 
 /* ---------------------------------------------------------------------- */
+/* context (prefill) attention: a chunk of T new tokens per sequence       */
+/* ---------------------------------------------------------------------- */
+/*
+ * The pages name a context-attention kernel ("prefix_prefill", Context
+ * Attention) next to the decode one but do not spell out what it computes;
+ * the plainest reading is taken: sequence b holds ctx_lens[b] cached keys,
+ * the last T of which belong to the chunk's tokens, and token t (absolute
+ * position ctx_lens[b] - T + t) attends causally to keys 0 .. its own
+ * position, with the same scaled, max-subtracted softmax as the decode step.
+ * T = 1 is exactly the decode step.
+ */
+typedef struct {
+  const uint16_t *q, *k, *v;
+  const int32_t* ctx_lens;
+  int B, T, Hq, Hkv, D, Lmax;
+  double scale;
+  double* ref;    /* [B, T, Hq*D] unrounded, or NULL */
+  uint16_t* out;  /* [B, T, Hq*D] bf16 words */
+  int err;
+} prefill_ctx;
+
+/* One unit = one (batch b, kv head h) pair: every token of the chunk and every
+ * query head of the group. */
+static void prefill_unit(void* p, long unit) {
+  prefill_ctx* c = (prefill_ctx*)p;
+  const int G = c->Hq / c->Hkv;
+  const int D = c->D;
+  const int b = (int)(unit / c->Hkv);
+  const int h = (int)(unit % c->Hkv);
+  const int ctx = c->ctx_lens[b];
+  const size_t kv_base = ((size_t)b * c->Hkv + h) * (size_t)c->Lmax * D;
+  double* s = (double*)malloc(sizeof(double) * (size_t)ctx);
+  if (!s) {
+    c->err = ORACLE_ENOMEM;
+    return;
+  }
+  for (int t = 0; t < c->T; t++) {
+    const int L = ctx - c->T + t + 1; /* keys up to and including the token's own position */
+    for (int g = 0; g < G; g++) {
+      const int qh = h * G + g;
+      const uint16_t* qrow = c->q + (((size_t)b * c->T + t) * c->Hq + qh) * D;
+      for (int j = 0; j < L; j++) {
+        const uint16_t* krow = c->k + kv_base + (size_t)j * D;
+        double dot = 0.0;
+        for (int d = 0; d < D; d++) dot += oracle_bf16_to_double(qrow[d]) * oracle_bf16_to_double(krow[d]);
+        s[j] = dot * c->scale;
+      }
+      double mx = s[0];
+      for (int j = 1; j < L; j++)
+        if (s[j] > mx) mx = s[j];
+      double Z = 0.0;
+      for (int j = 0; j < L; j++) {
+        s[j] = exp(s[j] - mx);
+        Z += s[j];
+      }
+      const size_t out_row = (((size_t)b * c->T + t) * c->Hq + qh) * D;
+      for (int d = 0; d < D; d++) {
+        double o = 0.0;
+        for (int j = 0; j < L; j++) o += (s[j] / Z) * oracle_bf16_to_double(c->v[kv_base + (size_t)j * D + d]);
+        if (c->ref) c->ref[out_row + d] = o;
+        c->out[out_row + d] = oracle_bf16_from_double(o);
+      }
+    }
+  }
+  free(s);
+}
+
+/*
+ * q [B, T, Hq, D], k/v [B, Hkv, Lmax, D] (bf16 words), ctx_lens [B] with
+ * T <= ctx_lens[b] <= Lmax. Writes out [B, T, Hq*D] (bf16 words) and, when
+ * non-NULL, the unrounded output.
+ */
+int oracle_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* ctx_lens,
+                             int B, int T, int Hq, int Hkv, int D, int Lmax, double scale, double* ref,
+                             uint16_t* out, int nthreads) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || D < 1 || Lmax < 1 || Hq % Hkv != 0) return ORACLE_EINVAL;
+  for (int b = 0; b < B; b++)
+    if (ctx_lens[b] < T || ctx_lens[b] > Lmax) return ORACLE_EINVAL;
+  prefill_ctx c = {.q = q, .k = k, .v = v, .ctx_lens = ctx_lens, .B = B, .T = T, .Hq = Hq, .Hkv = Hkv, .D = D,
+                   .Lmax = Lmax, .scale = scale, .ref = ref, .out = out, .err = 0};
+  int rc = run_units(prefill_unit, &c, (long)B * Hkv, nthreads);
+  return rc ? rc : c.err;
+}
+
+/* ---------------------------------------------------------------------- */
 /* output projection: [F16] third matmul, attn_output_flat x o_weight      */
 /* ---------------------------------------------------------------------- */
 

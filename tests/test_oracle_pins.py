@@ -390,3 +390,74 @@ def test_thread_count_does_not_change_results():
     b = oracle.decode_step(inp["q"], inp["k"], inp["v"], inp["seq_lens"], inp["o_weight"], nthreads=7)
     np.testing.assert_array_equal(a["out_ref"], b["out_ref"])
     np.testing.assert_array_equal(a["attn_ref"], b["attn_ref"])
+
+
+# ---- context (prefill) attention -----------------------------------------
+
+def _prefill_inputs(B, T, Hq, Hkv, ctx, Lmax, D=128, seed=0):
+    rng = np.random.default_rng(seed)
+    q = workloads.bf16_words_from_float(rng.standard_normal((B, T, Hq, D)).astype(np.float32))
+    k = workloads.bf16_words_from_float(rng.standard_normal((B, Hkv, Lmax, D)).astype(np.float32))
+    v = workloads.bf16_words_from_float(rng.standard_normal((B, Hkv, Lmax, D)).astype(np.float32))
+    return q, k, v, np.asarray(ctx, dtype=np.int32)
+
+
+def test_prefill_of_one_token_is_the_decode_step():
+    q, k, v, ctx = _prefill_inputs(2, 1, 8, 2, [37, 64], 64, seed=1)
+    pre = oracle.prefill_attention(q, k, v, ctx)
+    dec = oracle.attention(q[:, 0], k, v, ctx)
+    np.testing.assert_array_equal(pre["out"][:, 0], dec["flat"])
+    np.testing.assert_array_equal(pre["ref"][:, 0], dec["ref"])
+
+
+def test_every_prefill_row_is_a_decode_step_over_its_prefix():
+    # token t of sequence b sees exactly keys 0 .. ctx_b - T + t: the decode oracle on that prefix
+    B, T, Hq, Hkv = 2, 5, 4, 2
+    q, k, v, ctx = _prefill_inputs(B, T, Hq, Hkv, [9, 30], 32, seed=2)
+    pre = oracle.prefill_attention(q, k, v, ctx)
+    for t in range(T):
+        lens = ctx - T + t + 1
+        dec = oracle.attention(q[:, t], k, v, lens)
+        np.testing.assert_array_equal(pre["ref"][:, t], dec["ref"])
+
+
+def test_prefill_is_causal():
+    B, T, Hq, Hkv = 1, 6, 4, 1
+    q, k, v, ctx = _prefill_inputs(B, T, Hq, Hkv, [20], 24, seed=3)
+    base = oracle.prefill_attention(q, k, v, ctx)["ref"]
+    # a key/value past a token's position (and the cache rows past the context) never reach it
+    for pos in (16, 19, 20, 23):
+        k2, v2 = k.copy(), v.copy()
+        k2[0, 0, pos] = workloads.bf16_words_from_float(np.full(128, 3.0, np.float32))
+        v2[0, 0, pos] = workloads.bf16_words_from_float(np.full(128, 7.0, np.float32))
+        got = oracle.prefill_attention(q, k2, v2, ctx)["ref"]
+        first_seeing = pos - (20 - T)  # tokens t >= this index see position pos
+        for t in range(T):
+            if t < first_seeing:
+                np.testing.assert_array_equal(got[0, t], base[0, t])
+            else:
+                assert np.abs(got[0, t] - base[0, t]).max() > 1e-3
+
+
+def test_prefill_without_prefix_first_token_returns_its_value_row():
+    q, k, v, ctx = _prefill_inputs(2, 4, 8, 2, [4, 4], 8, seed=4)
+    out = oracle.prefill_attention(q, k, v, ctx)["out"]
+    for b in range(2):
+        for qh in range(8):
+            np.testing.assert_array_equal(out[b, 0, qh * 128:(qh + 1) * 128], v[b, qh // 4, 0])
+
+
+def test_prefill_ignores_the_order_of_the_prefix():
+    q, k, v, ctx = _prefill_inputs(1, 3, 4, 1, [40], 40, seed=5)
+    base = oracle.prefill_attention(q, k, v, ctx)["ref"]
+    perm = np.random.default_rng(6).permutation(37)  # positions 0..36 are the prefix
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 0, :37] = k[0, 0, perm]
+    v2[0, 0, :37] = v[0, 0, perm]
+    np.testing.assert_allclose(oracle.prefill_attention(q, k2, v2, ctx)["ref"], base, rtol=0, atol=1e-12)
+
+
+def test_prefill_rejects_a_chunk_longer_than_the_context():
+    q, k, v, _ = _prefill_inputs(1, 4, 4, 1, [4], 8)
+    with pytest.raises(oracle.OracleError):
+        oracle.prefill_attention(q, k, v, np.array([3], np.int32))
