@@ -8,7 +8,8 @@ raises.
 
 The names mirror the C entry points: ``decode_attn_fwd``, ``decode_attn_only``,
 ``oproj_fwd``, ``gemm_f16``, ``decode_attn_workspace_size``,
-``oproj_workspace_size``, ``decode_attn_plan``, ``decode_attn_status_str``.
+``oproj_workspace_size``, ``decode_attn_plan``, ``decode_attn_status_str``,
+``prefill_attn_fwd``.
 """
 from __future__ import annotations
 
@@ -40,6 +41,7 @@ EXPORTED = (
     "oproj_fwd",
     "gemm_f16",
     "decode_attn_status_str",
+    "prefill_attn_fwd",
 )
 
 
@@ -97,6 +99,11 @@ class DecodeAttnPlan(ctypes.Structure):
     ]
 
 
+class PrefillAttnShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "num_tokens", "num_q_heads", "num_kv_heads", "head_dim",
+                                              "max_seq_len")] + [("softmax_scale", ctypes.c_float)]
+
+
 class DecodeAttnError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -132,6 +139,8 @@ def load_library(path: str = LIB_PATH):
     lib.oproj_fwd.argtypes = [vp, vp, vp, i32, i32, i32, vp, sz, vp]
     lib.gemm_f16.restype = ctypes.c_int
     lib.gemm_f16.argtypes = [vp, vp, vp, i32, i32, i32, vp]
+    lib.prefill_attn_fwd.restype = ctypes.c_int
+    lib.prefill_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(PrefillAttnShape), vp]
     lib.decode_attn_status_str.restype = ctypes.c_char_p
     lib.decode_attn_status_str.argtypes = [ctypes.c_int]
     _lib = lib
@@ -306,6 +315,25 @@ def gemm_f16(a, b, c=None, stream=None):
     if rc != DA_OK:
         raise DecodeAttnError(rc, "gemm_f16")
     return c
+
+
+def prefill_attn_fwd(q, k_cache, v_cache, ctx_lens, out=None, softmax_scale: float = 0.0, stream=None):
+    """Context attention of a chunk: q [B, T, Hq, D] -> out [B, T, Hq*D] bf16 (token t attends causally
+    to keys 0 .. ctx_lens[b] - T + t)."""
+    torch = _check_dev("q", q, _torch().bfloat16)
+    _check_dev("k_cache", k_cache, torch.bfloat16)
+    _check_dev("v_cache", v_cache, torch.bfloat16)
+    _check_dev("ctx_lens", ctx_lens, torch.int32)
+    B, T, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((B, T, Hq * D), dtype=torch.bfloat16, device=q.device)
+    shape = PrefillAttnShape(B, T, Hq, Hkv, D, Lmax, float(softmax_scale))
+    rc = load_library().prefill_attn_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), ctx_lens.data_ptr(),
+                                         out.data_ptr(), ctypes.byref(shape), _stream_handle(stream))
+    if rc != DA_OK:
+        raise DecodeAttnError(rc, "prefill_attn_fwd")
+    return out
 
 
 class PreparedCall:

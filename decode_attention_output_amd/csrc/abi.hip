@@ -596,6 +596,37 @@ int gemm_f16(const void* a, const void* b, void* c, int32_t M, int32_t N, int32_
   return da::launch_gemm_f16(g, (hipStream_t)stream) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
+int prefill_attn_fwd(const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_lens, void* out,
+                     const prefill_attn_shape_t* s, void* stream) {
+  if (!s || !q || !k_cache || !v_cache || !ctx_lens || !out) return DA_ERR_NULL;
+  if (misaligned(q, 16) || misaligned(k_cache, 16) || misaligned(v_cache, 16) || misaligned(out, 16) ||
+      misaligned(ctx_lens, 4))
+    return DA_ERR_ALIGN;
+  if (s->batch < 1 || s->num_tokens < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 || s->max_seq_len < 1)
+    return DA_ERR_SHAPE;
+  if (s->head_dim != kHeadDim || s->num_q_heads % s->num_kv_heads != 0) return DA_ERR_SHAPE;
+  if (s->num_q_heads / s->num_kv_heads > DA_MAX_GROUP || s->num_tokens > s->max_seq_len) return DA_ERR_SHAPE;
+  if ((size_t)s->max_seq_len * kHeadDim * 2 >= (1ull << 32)) return DA_ERR_SHAPE;
+  const double rows = (double)s->batch * s->num_kv_heads * s->num_tokens * (s->num_q_heads / s->num_kv_heads);
+  if (rows / 64 > 2.0e9 || (double)s->batch * s->num_tokens * s->num_q_heads * kHeadDim > 9.0e15)
+    return DA_ERR_SHAPE;
+  da::PrefillParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k_cache;
+  p.v = (const uint16_t*)v_cache;
+  p.ctx_lens = ctx_lens;
+  p.out = (uint16_t*)out;
+  p.B = s->batch;
+  p.T = s->num_tokens;
+  p.Hq = s->num_q_heads;
+  p.Hkv = s->num_kv_heads;
+  p.G = s->num_q_heads / s->num_kv_heads;
+  p.Lmax = s->max_seq_len;
+  const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return da::launch_prefill(p, (hipStream_t)stream) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
 const char* decode_attn_status_str(int status) {
   switch (status) {
     case DA_OK: return "ok";

@@ -118,6 +118,18 @@ bool decode_step_supported(int gpad, int mpad, int tile_n);
 int decode_step_chunk(int tile_n);
 hipError_t launch_decode_step(const StepParams& p, int gpad, int mpad, int tile_n, hipStream_t s);
 
+// Context (prefill) attention of a chunk of T tokens per sequence, head_dim 128.
+struct PrefillParams {
+  const uint16_t* q;        // bf16 [B, T, Hq, 128]
+  const uint16_t* k;        // bf16 [B, Hkv, Lmax, 128]
+  const uint16_t* v;        // bf16 [B, Hkv, Lmax, 128]
+  const int32_t* ctx_lens;  // [B] keys per sequence, the chunk being the last T
+  uint16_t* out;            // bf16 [B, T, Hq*128]
+  int B, T, Hq, Hkv, G, Lmax;
+  float scale_log2;         // softmax scale * log2(e)
+};
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
+
 hipError_t launch_gemv(const GemvParams& p, int mpad, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_f16(const GemmParams& p, hipStream_t s);

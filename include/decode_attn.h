@@ -209,6 +209,37 @@ int oproj_fwd(const void* x_dev, const void* w_dev, void* out_dev, int32_t M, in
  */
 int gemm_f16(const void* a_dev, const void* b_dev, void* c_dev, int32_t M, int32_t N, int32_t K, void* stream);
 
+/*
+ * Context (prefill) attention of a chunk of new tokens. The F-16 page names a
+ * context-attention kernel beside the decode one without defining it; read
+ * plainly: sequence b holds ctx_lens[b] cached keys, the last num_tokens of
+ * which are the chunk's own tokens (already written to the caches), and token t
+ * attends causally to keys 0 .. ctx_lens[b] - num_tokens + t with the decode
+ * step's scaled softmax (num_tokens = 1 is decode_attn_only).
+ *
+ *  q_dev         bf16 [B, T, Hq, D] (T = num_tokens, token-major)
+ *  k_cache_dev   bf16 [B, Hkv, Lmax, D]
+ *  v_cache_dev   bf16 [B, Hkv, Lmax, D]
+ *  ctx_lens_dev  int32 [B], each in [T, Lmax] (precondition, not checked on the
+ *                device; a value outside it gives undefined results)
+ *  out_dev       bf16 [B, T, Hq*D], head-major within a token as in decode
+ * head_dim 128 only; softmax_scale 0 selects 1/sqrt(head_dim). No workspace.
+ * Returns DA_OK or a DA_ERR_* code (checks before any HIP call).
+ */
+typedef struct {
+  int32_t batch;
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_seq_len;
+  float softmax_scale;
+} prefill_attn_shape_t;
+
+int prefill_attn_fwd(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                     const int32_t* ctx_lens_dev, void* out_dev, const prefill_attn_shape_t* shape,
+                     void* stream);
+
 /* Static text for a status code. */
 const char* decode_attn_status_str(int status);
 

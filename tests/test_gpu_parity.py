@@ -326,3 +326,54 @@ def test_head_dim_256_single_key_is_bit_exact(gpu):
     for b in range(2):
         for qh in range(8):
             np.testing.assert_array_equal(res["flat"][b, qh * 256:(qh + 1) * 256], inp["v"][b, qh // 4, 0])
+
+
+# ---- context (prefill) attention ------------------------------------------
+
+def _prefill_case(B, T, Hq, Hkv, ctx, Lmax, seed):
+    rng = np.random.default_rng(seed)
+    q = workloads.bf16_words_from_float(rng.standard_normal((B, T, Hq, 128)).astype(np.float32))
+    k = workloads.bf16_words_from_float(rng.standard_normal((B, Hkv, Lmax, 128)).astype(np.float32))
+    v = workloads.bf16_words_from_float(rng.standard_normal((B, Hkv, Lmax, 128)).astype(np.float32))
+    workloads.poison_padding(k, v, ctx)  # rows past each context are NaN: never read
+    return q, k, v, np.asarray(ctx, dtype=np.int32)
+
+
+PREFILL = [
+    # (batch, tokens, Hq, Hkv, ctx_lens, max_seq_len)
+    (1, 1, 4, 1, [5], 8),
+    (1, 17, 8, 2, [17], 20),
+    (2, 40, 32, 8, [100, 40], 128),
+    (1, 64, 16, 1, [300], 300),
+    (2, 5, 2, 2, [33, 7], 40),
+    (3, 33, 24, 8, [1000, 500, 33], 1024),
+    (1, 256, 32, 8, [2048], 2048),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: "B%d_T%d_H%d_KV%d_ctx%s" % (c[0], c[1], c[2], c[3],
+                                                                                     "-".join(map(str, c[4]))))
+def test_prefill_matches_the_oracle(gpu, case):
+    B, T, Hq, Hkv, ctx, Lmax = case
+    q, k, v, cl = _prefill_case(B, T, Hq, Hkv, ctx, Lmax, seed=500 + T + Hq)
+    out = host_words(da.prefill_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(cl)))
+    ref = oracle.prefill_attention(q, k, v, cl)
+    assert_bf16_close(out, ref["ref"], "prefill %s" % (case,))
+
+
+def test_prefill_first_token_without_prefix_is_bit_exact(gpu):
+    q, k, v, cl = _prefill_case(2, 9, 8, 2, [9, 9], 16, seed=61)
+    out = host_words(da.prefill_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(cl)))
+    for b in range(2):
+        for qh in range(8):
+            np.testing.assert_array_equal(out[b, 0, qh * 128:(qh + 1) * 128], v[b, qh // 4, 0])
+
+
+def test_prefill_of_one_token_matches_decode_attention(gpu):
+    q, k, v, cl = _prefill_case(3, 1, 16, 4, [70, 1, 129], 130, seed=62)
+    pre = host_words(da.prefill_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_i32(cl)))
+    dec = host_words(da.decode_attn_only(dev_bf16(q[:, 0]), dev_bf16(k), dev_bf16(v), dev_i32(cl)))
+    # both within the bound of the same oracle; equal up to their different summation orders
+    ref = oracle.attention(q[:, 0], k, v, cl)["ref"]
+    assert_bf16_close(pre[:, 0], ref, "prefill T=1")
+    assert_bf16_close(dec, ref, "decode")
