@@ -32,6 +32,8 @@ METRIC = "µs per decode step (attn+o_proj) and achieved HBM TB/s vs peak, 1×MI
 CALIB_BYTES = 64 * 2 ** 20  # plain device-to-device copy whose HBM traffic is known (read + write)
 PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
+PREFILL_METRIC = "TFLOP/s of context (prefill) attention of a token chunk vs bf16 MFMA peak, 1×MI355X"
 MALL_BYTES = 256 * 1024 * 1024
 
 
@@ -90,6 +92,13 @@ def dominant_kernel(wl, plan, seq_lens):
     return "attn_streamk_kernel", attn_bytes, "attention"
 
 
+def prefill_alg_bytes(wl):
+    """Bytes a chunk's attention must move at minimum: its queries, every cached
+    K and V row once, and its bf16 output."""
+    rows = wl.batch * wl.tokens * wl.num_q_heads * wl.head_dim
+    return 2 * rows + 2 * 2 * wl.batch * wl.num_kv_heads * wl.ctx_len * wl.head_dim + 2 * rows
+
+
 def summarize_profile(args):
     """profiles/<kernel>_<workload>.txt from a FETCH_SIZE run, a WRITE_SIZE run and a kernel-trace run."""
     import csv
@@ -99,10 +108,14 @@ def summarize_profile(args):
     import workloads
 
     wl = workloads.BY_NAME[args.workload]
-    s = wl.shape
-    seq_lens = workloads.draw_seq_lens(wl, np.random.default_rng(wl.seed))
-    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden, s.head_dim))
-    kname, kbytes, _ = dominant_kernel(wl, plan, seq_lens)
+    if isinstance(wl, workloads.PrefillWorkload):
+        kname, kbytes = "prefill_kernel", prefill_alg_bytes(wl)
+    else:
+        s = wl.shape
+        seq_lens = workloads.draw_seq_lens(wl, np.random.default_rng(wl.seed))
+        plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden,
+                                                 s.head_dim))
+        kname, kbytes, _ = dominant_kernel(wl, plan, seq_lens)
 
     def counter_avg(path, counter, match):
         vals = []
@@ -168,7 +181,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=workloads.PAGES.name, choices=[w.name for w in workloads.DECODE])
+    ap.add_argument("--workload", default=workloads.PAGES.name,
+                    choices=[w.name for w in workloads.DECODE + workloads.PREFILL])
     ap.add_argument("--min-rotate-mib", type=float, default=512.0)
     ap.add_argument("--breakdown-steps", type=int, default=400, help="launches per kernel in the breakdown pass")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
@@ -198,6 +212,9 @@ def main():
     import workloads
 
     wl = workloads.BY_NAME[args.workload]
+    if isinstance(wl, workloads.PrefillWorkload):
+        bench_prefill(args, wl)
+        return
     s = wl.shape
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -379,6 +396,132 @@ def main():
             "cores": threads,
             "kind": "oracle",
             "sample": "%d full decode steps of %s (fp64 C oracle, %d threads, %.1f s)" % (n, wl.name, threads, t_cpu),
+        }
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args, wl):
+    """One step = the attention of one token chunk of every sequence (one launch)."""
+    import numpy as np
+    import torch
+
+    import decode_attention_output_amd as da
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    da.load_library()
+    inp = workloads.prefill_inputs(wl, poison=True)
+    ctx = inp["ctx_lens"]
+    flops = workloads.prefill_flops(wl.tokens, wl.num_q_heads, wl.head_dim, ctx)
+    nbytes = prefill_alg_bytes(wl)
+
+    def to_dev(words):
+        return torch.from_numpy(np.ascontiguousarray(words).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = {n: to_dev(inp[n]) for n in ("q", "k", "v")}
+    cl = torch.from_numpy(ctx).to(dev)
+    R = max(1, math.ceil(args.min_rotate_mib * 2 ** 20 / nbytes))
+    sets = []
+    for r in range(R):
+        st = {n: (t if r == 0 else t.clone()) for n, t in base.items()}
+        st["out"] = torch.empty((wl.batch, wl.tokens, wl.num_q_heads * wl.head_dim), dtype=torch.bfloat16,
+                                device=dev)
+        sets.append(st)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(stream)
+
+    def step(st):
+        da.prefill_attn_fwd(st["q"], st["k"], st["v"], cl, out=st["out"], stream=stream)
+
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(sets[i % R])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) / args.steps * 1e6
+    gpu_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    step(sets[0])
+    torch.cuda.synchronize()
+
+    # the elementwise copy whose counters scale a profiled run's HBM bytes
+    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    torch.mul(calib_src, 1.0, out=calib_dst)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
+
+    achieved = flops / (gpu_us * 1e-6) / 1e12
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": round(flops / (wall_us * 1e-6) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_us / 1e3, 6),
+        "us_per_step": round(wall_us, 3),
+        "us_per_step_gpu_events": round(gpu_us, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "tokens": wl.tokens, "num_q_heads": wl.num_q_heads,
+            "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "ctx_len": wl.ctx_len,
+            "algorithmic_flops": flops, "algorithmic_bytes": nbytes, "rotation_sets": R,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_kernel",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_from_profile(wl.name, "prefill_kernel"),
+            "avg_launch_us": round(gpu_us, 3),
+            "alg_flops_per_launch": flops,
+            "timing": "HIP events around the timed steps (one launch each) on the bench stream",
+        },
+    }
+    if not args.no_parity or not args.no_cpu_baseline:
+        # one bounded oracle sample serves both: the first sequence's chunk (its
+        # output is compared element by element, and the runs are timed)
+        import oracle
+
+        threads = oracle.default_threads()
+        sub = {n: np.ascontiguousarray(inp[n][:1]) for n in ("q", "k", "v")}
+        sub_flops = workloads.prefill_flops(wl.tokens, wl.num_q_heads, wl.head_dim, ctx[:1])
+        n, t_cpu, ref = 0, 0.0, None
+        while n < 1 or (not args.no_cpu_baseline and t_cpu < args.cpu_seconds and n < 100):
+            c0 = time.perf_counter()
+            ref = oracle.prefill_attention(sub["q"], sub["k"], sub["v"], ctx[:1], nthreads=threads)["ref"]
+            t_cpu += time.perf_counter() - c0
+            n += 1
+    if not args.no_parity:
+        got = torch.from_numpy(sets[0]["out"][:1].cpu().view(torch.int16).numpy()).view(torch.bfloat16)
+        got = got.double().numpy()
+        err = np.abs(got - ref)
+        mask = np.abs(ref) >= 1e-2
+        rel = float((err[mask] / np.abs(ref[mask])).max()) if mask.any() else 0.0
+        ok = bool(np.all(np.isfinite(got)) and err.max() <= 1e-2 and rel <= 2.0 ** -7)
+        result["parity"] = {"vs": "oracle", "ok": ok, "max_abs": float(err.max()), "max_rel": rel,
+                            "checked": "every output of the first sequence's chunk"}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = {
+            "value": round(sub_flops * n / t_cpu / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": threads,
+            "kind": "oracle",
+            "sample": "%d run(s) of the first sequence's %d-token chunk of %s (fp64 C oracle, %d threads, %.1f s)"
+                      % (n, wl.tokens, wl.name, threads, t_cpu),
         }
     print(json.dumps(result), flush=True)
 

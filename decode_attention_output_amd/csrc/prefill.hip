@@ -8,15 +8,22 @@
 // scaled softmax (T = 1 is the decode attention).
 //
 // Many query rows share every key, so this is a real MFMA contraction. A
-// workgroup owns 64 query rows of one (batch, kv head) -- row r is token
-// r / G, query head r % G of the group -- 16 per wave, which is exactly the
-// B operand (16 columns) of the decode step's S^T = K x Q^T product. The four
-// waves share each 32-key K/V tile: the workgroup loads it cooperatively
-// (1 KiB per load instruction, whole rows) into one of two LDS stages while
-// the waves compute the previous tile with the per-wave step of attn_core.hpp
-// (online softmax, P x V with fp32-exact weights), each lane masking the keys
-// past its own row's position. A wave stops computing once every key of its
-// rows is done; the workgroup stops loading at the last key of its last row.
+// workgroup owns 4 * 16 * kRowSets query rows of one (batch, kv head) -- row r
+// is token r / G, query head r % G of the group -- and each wave kRowSets sets
+// of 16 rows, every set one 16-column B operand of S^T = K x Q^T: each K and V
+// operand read from LDS feeds kRowSets products. The four waves share each
+// 32-key K/V tile: the workgroup loads it cooperatively (whole rows, 1 KiB per
+// load instruction) into one of two LDS stages while the waves compute the
+// previous tile (online softmax with a lazy rescale, each lane masking the keys
+// past its own row's position). A wave skips the tiles past the last key of its
+// rows; the workgroup stops loading at the last key of its last row; the
+// workgroups of the longest rows (the end of the chunk) start first.
+//
+// The weights enter P x V as two bf16 terms (truncated high part, then the
+// rounded rest): together they carry 16 significant bits, a relative error of at
+// most 2^-17 per weight, which is the accuracy its fp32 score itself has after
+// the 128-term dot product; the decode kernels keep three (fp32-exact weights)
+// because there the matrix cores are idle anyway.
 #include "attn_core.hpp"
 #include "kernels.hpp"
 
@@ -26,8 +33,109 @@ namespace {
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
-constexpr int kPrefillRows = kPrefillWaves * 16;  // query rows per workgroup
-constexpr int kPrefillLds = 2 * kStageBytes;      // two K/V stages shared by the waves
+constexpr int kRowSets = 2;                                // 16-row sets per wave
+constexpr int kPrefillRows = kPrefillWaves * 16 * kRowSets;  // query rows per workgroup
+constexpr int kPrefillLds = 2 * kStageBytes;               // two K/V stages shared by the waves
+
+template <int RS>
+struct PrefillWave {
+  f32x4_t o[RS][8];  // set s: O[row 4g + r][dim 16j + lane%16] in element r of o[s][j]
+  float m_ref[RS];   // reference max (log2 units) of row lane%16 of each set
+  float l_acc[RS];   // this lane's share of that row's weight sum
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// One 32-key step of a wave's RS row sets on the K/V tile in `stage`. With
+// MASK, key k is dropped for row lane%16 of set s unless k < end[s] (the tiles
+// that cross the causal diagonal); without it every key of the tile counts.
+// Every row has at least key 0, so its first tile gives it a finite max.
+template <int RS, bool MASK>
+__device__ __forceinline__ void prefill_step(PrefillWave<RS>& w, const char* stage, const uint4 (&qb)[RS][4],
+                                             int key0, const int (&end)[RS], float scale_log2, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  // ---- S^T = K x Q^T: lane (i, g) gets the scores of row i for keys 16tt + 4g + r ----
+  f32x4_t sc[RS][2];
+#pragma unroll
+  for (int s = 0; s < RS; ++s)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) sc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const char* kr = stage + (16 * tt + i) * kStageRow + g * 16;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 a = *reinterpret_cast<const uint4*>(kr + kk * 64);
+#pragma unroll
+      for (int s = 0; s < RS; ++s) sc[s][tt] = mfma_bf16(a, qb[s][kk], sc[s][tt]);
+    }
+  }
+
+  // ---- online softmax per set (max on the raw scores, the scale > 0 keeps the
+  // order), then the weights as two bf16 terms of the P x V A operand:
+  // k index 8g + e is key 4g + e (e < 4), then 16 + 4g + e - 4 ----
+  uint4 pa[RS][2];
+#pragma unroll
+  for (int s = 0; s < RS; ++s) {
+    float x[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        x[tt][r] = (!MASK || key0 + 16 * tt + 4 * g + r < end[s]) ? sc[s][tt][r] : -INFINITY;
+    // the reference moves only when some lane's own scores pass it by the
+    // slack: the row max over the four lanes of a row is taken only then
+    const float lm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                           fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    if (__builtin_amdgcn_ballot_w64(lm * scale_log2 > w.m_ref[s] + kRescaleSlack) != 0) {
+      float mx = fmaxf(lm, __shfl_xor(lm, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+      const float mn = fmaxf(w.m_ref[s], mx);
+      const float alpha = __builtin_amdgcn_exp2f(w.m_ref[s] - mn);  // 0 while the reference is -inf
+      w.m_ref[s] = mn;
+      w.l_acc[s] *= alpha;
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w.o[s][j][r] *= ar[r];
+    }
+    const float neg_m = -w.m_ref[s];
+    float p[2][4], rest[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // a dropped key: exp2(-inf) = 0
+        p[tt][r] = __builtin_amdgcn_exp2f(fmaf(x[tt][r], scale_log2, neg_m));
+        w.l_acc[s] += p[tt][r];
+        rest[tt][r] = p[tt][r] - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p[tt][r]) & 0xffff0000u);
+      }
+    auto lo2 = [](float a, float b) {
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));  // round to nearest even
+    };
+    pa[s][0] = make_uint4(pack_hi(p[0][0], p[0][1]), pack_hi(p[0][2], p[0][3]), pack_hi(p[1][0], p[1][1]),
+                          pack_hi(p[1][2], p[1][3]));
+    pa[s][1] = make_uint4(lo2(rest[0][0], rest[0][1]), lo2(rest[0][2], rest[0][3]), lo2(rest[1][0], rest[1][1]),
+                          lo2(rest[1][2], rest[1][3]));
+  }
+
+  // ---- O += P x V, 16 dims per product; each V operand serves every set and term ----
+  const char* vt = stage + kStageTile + (4 * g + (i >> 2)) * kStageRow + (i & 3) * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint2 v0 = lds_read_tr16(vt + j * 32);
+    const uint2 v1 = lds_read_tr16(vt + 16 * kStageRow + j * 32);
+    const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+    for (int s = 0; s < RS; ++s)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) w.o[s][j] = mfma_bf16(pa[s][e], vb, w.o[s][j]);
+  }
+}
 
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kPrefillLds];
@@ -35,38 +143,38 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   const int i = lane & 15, grp = lane >> 4;
   const int R = p.T * p.G;                        // query rows of one (batch, kv head)
   const int blocks = (R + kPrefillRows - 1) / kPrefillRows;
-  const int blk = blockIdx.x % blocks;
-  const int seq = blockIdx.x / blocks;            // (batch, kv head)
+  const int nseq = p.B * p.Hkv;
+  // the last blocks of every sequence (longest rows) first; consecutive
+  // workgroups take different sequences
+  const int blk = blocks - 1 - (int)(blockIdx.x / nseq);
+  const int seq = blockIdx.x % nseq;              // (batch, kv head)
   const int b = seq / p.Hkv, h = seq % p.Hkv;
   const int ctx = min(max(p.ctx_lens[b], 0), p.Lmax);
   const int base = ctx - p.T;                     // position of the chunk's first token
 
-  // ---- this wave's 16 rows: the query (B operand) and the number of keys each row sees ----
-  const int r0 = blk * kPrefillRows + wave * 16;
-  const int rr = r0 + i;                          // the row of this lane's column
-  const int tok = rr / p.G, gq = rr % p.G;
-  const bool row_ok = rr < R;
-  uint4 qb[4];
-  const uint16_t* qrow = p.q + (((size_t)b * p.T + tok) * p.Hq + (size_t)h * p.G + gq) * kHeadDim;
+  // ---- this wave's rows: the queries (B operands) and the number of keys each row sees ----
+  const int r0 = blk * kPrefillRows + wave * 16 * kRowSets;
+  uint4 qb[kRowSets][4];
+  int end[kRowSets];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qb[kk] = row_ok ? ld16(qrow + kk * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
-  const int end = row_ok ? base + tok + 1 : 0;    // keys 0 .. end-1
-  // keys of the wave's last row and of the workgroup's last row
-  const int wave_last = min(r0 + 15, R - 1), blk_last = min(blk * kPrefillRows + kPrefillRows - 1, R - 1);
-  const int wave_keys = r0 < R ? base + wave_last / p.G + 1 : 0;
-  const int blk_keys = base + blk_last / p.G + 1;
+  for (int s = 0; s < kRowSets; ++s) {
+    const int rr = r0 + 16 * s + i;
+    const bool ok = rr < R;
+    const int tok = rr / p.G, gq = rr % p.G;
+    const uint16_t* qrow = p.q + (((size_t)b * p.T + tok) * p.Hq + (size_t)h * p.G + gq) * kHeadDim;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[s][kk] = ok ? ld16(qrow + kk * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
+    end[s] = ok ? base + tok + 1 : 1;             // keys 0 .. end-1 (a row past the end: key 0, not stored)
+  }
+  // keys of the wave's first and last rows, and of the workgroup's last row
+  const int wave_first_keys = r0 < R ? base + r0 / p.G + 1 : 0;
+  const int wave_keys = r0 < R ? base + min(r0 + 16 * kRowSets - 1, R - 1) / p.G + 1 : 0;
+  const int blk_keys = base + min(blk * kPrefillRows + kPrefillRows - 1, R - 1) / p.G + 1;
   const int ntiles = (blk_keys + kStepKeys - 1) / kStepKeys;
 
-  AttnSeg sg;
   const size_t kv_off = (size_t)seq * p.Lmax * kHeadDim;
-  sg.K = make_rsrc(p.k + kv_off, (uint32_t)ctx * kRowBytes);  // rows past the context read as 0
-  sg.V = make_rsrc(p.v + kv_off, (uint32_t)ctx * kRowBytes);
-  sg.L = ctx;
-  sg.G = p.G;
-  sg.scale_log2 = p.scale_log2;
-  sg.scale = 0.f;
-  sg.dbg = nullptr;
-  sg.dbg_stride = 0;
+  const rsrc_t K = make_rsrc(p.k + kv_off, (uint32_t)ctx * kRowBytes);  // rows past the context read as 0
+  const rsrc_t V = make_rsrc(p.v + kv_off, (uint32_t)ctx * kRowBytes);
 
   // ---- the shared K/V tiles: thread t loads rows t/16 and 16 + t/16, bytes (t%16)*16 ----
   uint4 kr[2], vr[2];
@@ -74,8 +182,8 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
     const uint32_t off = (uint32_t)(tile * kStepKeys + t / 16) * kRowBytes + (t % 16) * 16;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      kr[j] = rsrc_ld16(sg.K, off + j * 16 * kRowBytes);
-      vr[j] = rsrc_ld16(sg.V, off + j * 16 * kRowBytes);
+      kr[j] = rsrc_ld16(K, off + j * 16 * kRowBytes);
+      vr[j] = rsrc_ld16(V, off + j * 16 * kRowBytes);
     }
   };
   auto store_tile = [&](char* stage) {
@@ -87,8 +195,14 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
     }
   };
 
-  AttnWave aw;
-  aw.reset();
+  PrefillWave<kRowSets> aw;
+#pragma unroll
+  for (int s = 0; s < kRowSets; ++s) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) aw.o[s][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    aw.m_ref[s] = -INFINITY;
+    aw.l_acc[s] = 0.f;
+  }
   if (ntiles > 0) load_tile(0);
   for (int tile = 0; tile < ntiles; ++tile) {
     char* stage = smem + (tile & 1) * kStageBytes;
@@ -96,22 +210,29 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
     store_tile(stage);
     __syncthreads();
     if (tile + 1 < ntiles) load_tile(tile + 1);
-    if (tile * kStepKeys < wave_keys) attn_step<16>(aw, stage, qb, sg, tile * kStepKeys, end, lane);
+    const int key0 = tile * kStepKeys;
+    if (key0 + kStepKeys <= wave_first_keys)
+      prefill_step<kRowSets, false>(aw, stage, qb, key0, end, p.scale_log2, lane);
+    else if (key0 < wave_keys)
+      prefill_step<kRowSets, true>(aw, stage, qb, key0, end, p.scale_log2, lane);
   }
 
-  // ---- normalise and store: element r of o[j] is row 4*grp + r, dim 16j + i ----
-  float l = aw.l_acc;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);  // lane i (every group) holds the weight sum of its column's row
+  // ---- normalise and store: element r of o[s][j] is row 16s + 4*grp + r, dim 16j + i ----
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int q = 4 * grp + r;
-    const int row = r0 + q;
-    const float inv = 1.f / __shfl(l, q);
-    if (row >= R) continue;
-    uint16_t* orow = p.out + (((size_t)b * p.T + row / p.G) * p.Hq + (size_t)h * p.G + row % p.G) * kHeadDim;
+  for (int s = 0; s < kRowSets; ++s) {
+    float l = aw.l_acc[s];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);  // lane i (every group) holds the weight sum of its set's row i
 #pragma unroll
-    for (int j = 0; j < 8; ++j) orow[16 * j + i] = f32_to_bf16_rne(aw.o[j][r] * inv);
+    for (int r = 0; r < 4; ++r) {
+      const int q = 4 * grp + r;
+      const int row = r0 + 16 * s + q;
+      const float inv = 1.f / __shfl(l, q);
+      if (row >= R) continue;
+      uint16_t* orow = p.out + (((size_t)b * p.T + row / p.G) * p.Hq + (size_t)h * p.G + row % p.G) * kHeadDim;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) orow[16 * j + i] = f32_to_bf16_rne(aw.o[s][j][r] * inv);
+    }
   }
 }
 

@@ -51,6 +51,24 @@ class DecodeWorkload:
 
 
 @dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    """A chunk of ``tokens`` new tokens per sequence appended to a cache of
+    ``ctx_len`` keys in all (the chunk being the last ``tokens`` of them)."""
+    name: str
+    batch: int
+    tokens: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    ctx_len: int
+    seed: int
+
+    @property
+    def max_seq_len(self) -> int:
+        return self.ctx_len
+
+
+@dataclasses.dataclass(frozen=True)
 class GemmWorkload:
     name: str
     m: int
@@ -74,9 +92,16 @@ LONG = DecodeWorkload("decode_b4_h64kv8_L32768_o8192", DecodeShape(4, 64, 8, 128
 WIDE = DecodeWorkload("decode_b4_h16kv2_d256_L16384_o4096", DecodeShape(4, 16, 2, 256, 16384, 4096), seed=5,
                       seq_len=16384)
 
-ALL = [TINY, PAGES, GEMM, BATCHED, LONG, WIDE]
+# Context (prefill) attention of the same model shape (32 query / 8 KV heads,
+# head_dim 128): a whole 2048-token prompt, and a 512-token chunk of each of 4
+# sequences behind a 7680-key prefix.
+PROMPT = PrefillWorkload("prefill_b1_t2048_h32kv8_ctx2048", 1, 2048, 32, 8, 128, 2048, seed=6)
+CHUNK = PrefillWorkload("prefill_b4_t512_h32kv8_ctx8192", 4, 512, 32, 8, 128, 8192, seed=7)
+
+ALL = [TINY, PAGES, GEMM, BATCHED, LONG, WIDE, PROMPT, CHUNK]
 BY_NAME = {w.name: w for w in ALL}
 DECODE = [TINY, PAGES, BATCHED, LONG, WIDE]
+PREFILL = [PROMPT, CHUNK]
 
 
 def _to_bf16_words(x: np.ndarray) -> np.ndarray:
@@ -141,6 +166,27 @@ def custom_decode_inputs(batch: int, num_q_heads: int, num_kv_heads: int, seq_le
     if poison:
         poison_padding(k, v, sl)
     return {"seq_lens": sl, "q": q, "k": k, "v": v, "o_weight": w, "shape": s}
+
+
+def prefill_inputs(wl: PrefillWorkload, poison: bool = True) -> dict:
+    """Draw (q, k, v) in that order from default_rng(seed): q ~ N(0,1)
+    [B,T,Hq,D], k, v ~ N(0,1) [B,Hkv,ctx_len,D]; every sequence holds ctx_len keys."""
+    rng = np.random.default_rng(wl.seed)
+    ctx = np.full(wl.batch, wl.ctx_len, dtype=np.int32)
+    q = _normal_bf16(rng, (wl.batch, wl.tokens, wl.num_q_heads, wl.head_dim))
+    k = _normal_bf16(rng, (wl.batch, wl.num_kv_heads, wl.max_seq_len, wl.head_dim))
+    v = _normal_bf16(rng, (wl.batch, wl.num_kv_heads, wl.max_seq_len, wl.head_dim))
+    if poison:
+        poison_padding(k, v, ctx)
+    return {"ctx_lens": ctx, "q": q, "k": k, "v": v}
+
+
+def prefill_flops(tokens: int, num_q_heads: int, head_dim: int, ctx_lens) -> int:
+    """Multiply-adds x 2 of a chunk's attention: every (token, query head) row
+    of sequence b meets ctx_lens[b] - tokens + t + 1 keys, and each key costs
+    head_dim products for its score and head_dim for its share of the output."""
+    keys = sum(int(c) * tokens - tokens * (tokens - 1) // 2 for c in np.asarray(ctx_lens))
+    return 4 * head_dim * num_q_heads * keys
 
 
 def gemm_inputs(wl: GemmWorkload = GEMM, all_ones: bool = False) -> dict:
