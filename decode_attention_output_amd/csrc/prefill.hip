@@ -13,11 +13,13 @@
 // of 16 rows, every set one 16-column B operand of S^T = K x Q^T: each K and V
 // operand read from LDS feeds kRowSets products. The four waves share each
 // 32-key K/V tile: the workgroup loads it cooperatively (whole rows, 1 KiB per
-// load instruction) into one of two LDS stages while the waves compute the
-// previous tile (online softmax with a lazy rescale, each lane masking the keys
-// past its own row's position). A wave skips the tiles past the last key of its
-// rows; the workgroup stops loading at the last key of its last row; the
-// workgroups of the longest rows (the end of the chunk) start first.
+// load instruction) and stores it into one of three LDS stages a tile ahead of
+// the waves, which compute the scores of the next tile while they turn the
+// current tile's scores into weights (online softmax with a lazy rescale, each
+// lane masking the keys past its own row's position) and multiply them into
+// O. A wave skips the tiles past the last key of its rows; the workgroup stops
+// loading at the last key of its last row; the workgroups of the longest rows
+// (the end of the chunk) start first.
 //
 // The weights enter P x V as two bf16 terms (truncated high part, then the
 // rounded rest): together they carry 16 significant bits, a relative error of at
@@ -35,7 +37,25 @@ constexpr int kPrefillWaves = 4;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr int kRowSets = 2;                                // 16-row sets per wave
 constexpr int kPrefillRows = kPrefillWaves * 16 * kRowSets;  // query rows per workgroup
-constexpr int kPrefillLds = 2 * kStageBytes;               // two K/V stages shared by the waves
+constexpr int kPrefillStages = 3;                          // K/V stages shared by the waves
+// A stage holds a 32-key K tile and V tile. K rows are read 16 bytes a lane,
+// 16 rows per 16 lanes: a 272-byte row stride puts the rows on distinct banks.
+// V rows are read by transposing 8-byte reads, 4 rows x 32 bytes per 16
+// lanes: a 288-byte stride spreads those rows over the banks.
+constexpr int kKRow = kRowBytes + 16;
+constexpr int kVRow = kRowBytes + 32;
+constexpr int kKTileBytes = kStepKeys * kKRow;
+constexpr int kPStageBytes = kKTileBytes + kStepKeys * kVRow;
+constexpr int kPrefillLds = kPrefillStages * kPStageBytes;
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+
+// Transposing LDS read of four 16-bit elements at an LDS address.
+__device__ __forceinline__ uint2 lds_tr16_at(const lds_char* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)const_cast<lds_char*>(p)));
+}
 
 template <int RS>
 struct PrefillWave {
@@ -47,47 +67,51 @@ struct PrefillWave {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// One 32-key step of a wave's RS row sets on the K/V tile in `stage`. With
-// MASK, key k is dropped for row lane%16 of set s unless k < end[s] (the tiles
-// that cross the causal diagonal); without it every key of the tile counts.
-// Every row has at least key 0, so its first tile gives it a finite max.
-template <int RS, bool MASK>
-__device__ __forceinline__ void prefill_step(PrefillWave<RS>& w, const char* stage, const uint4 (&qb)[RS][4],
-                                             int key0, const int (&end)[RS], float scale_log2, int lane) {
+// The three parts of a wave's 32-key step on a K/V tile, for RS row sets.
+//
+// Scores: S^T = K x Q^T; lane (i, g) gets the scores of row i for keys
+// 16tt + 4g + r of the tile in sc[s][tt][r].
+template <int RS>
+__device__ __forceinline__ void prefill_scores(f32x4_t (&sc)[RS][2], const lds_char* stage, const uint4 (&qb)[RS][4],
+                                               int lane) {
   const int i = lane & 15, g = lane >> 4;
-  // ---- S^T = K x Q^T: lane (i, g) gets the scores of row i for keys 16tt + 4g + r ----
-  f32x4_t sc[RS][2];
 #pragma unroll
   for (int s = 0; s < RS; ++s)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) sc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const char* kr = stage + (16 * tt + i) * kStageRow + g * 16;
+    const lds_char* kr = stage + (16 * tt + i) * kKRow + g * 16;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint4 a = *reinterpret_cast<const uint4*>(kr + kk * 64);
+      const uint4 a = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(kr + kk * 64));
 #pragma unroll
       for (int s = 0; s < RS; ++s) sc[s][tt] = mfma_bf16(a, qb[s][kk], sc[s][tt]);
     }
   }
+}
 
-  // ---- online softmax per set (max on the raw scores, the scale > 0 keeps the
-  // order), then the weights as two bf16 terms of the P x V A operand:
-  // k index 8g + e is key 4g + e (e < 4), then 16 + 4g + e - 4 ----
-  uint4 pa[RS][2];
+// Reference: with MASK, key k of the tile is dropped (score -inf) for row
+// lane%16 of set s unless k < end[s] (tiles that cross the causal diagonal).
+// The reference max moves only when some lane's own scores pass it by the
+// slack; only then is the row max over the four lanes of a row taken and the
+// accumulators rescaled. Every row has key 0, so its first tile gives it a
+// finite reference.
+template <int RS, bool MASK>
+__device__ __forceinline__ void prefill_reference(PrefillWave<RS>& w, const f32x4_t (&sc)[RS][2],
+                                                  float (&x)[RS][2][4], int key0, const int (&end)[RS],
+                                                  float scale_log2, int lane) {
+  const int g = lane >> 4;
 #pragma unroll
   for (int s = 0; s < RS; ++s) {
-    float x[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        x[tt][r] = (!MASK || key0 + 16 * tt + 4 * g + r < end[s]) ? sc[s][tt][r] : -INFINITY;
-    // the reference moves only when some lane's own scores pass it by the
-    // slack: the row max over the four lanes of a row is taken only then
-    const float lm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                           fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+        x[s][tt][r] = (!MASK || key0 + 16 * tt + 4 * g + r < end[s]) ? sc[s][tt][r] : -INFINITY;
+    // a chain of three-input maxima
+    const float lm = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(x[s][0][0], x[s][0][1]), x[s][0][2]), x[s][0][3]),
+                                             x[s][1][0]), x[s][1][1]), x[s][1][2]), x[s][1][3]);
     if (__builtin_amdgcn_ballot_w64(lm * scale_log2 > w.m_ref[s] + kRescaleSlack) != 0) {
       float mx = fmaxf(lm, __shfl_xor(lm, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
@@ -103,6 +127,17 @@ __device__ __forceinline__ void prefill_step(PrefillWave<RS>& w, const char* sta
 #pragma unroll
         for (int r = 0; r < 4; ++r) w.o[s][j][r] *= ar[r];
     }
+  }
+}
+
+// Weights: p = 2^(x * scale_log2 - reference), summed into the row's weight
+// sum and written as two bf16 terms of the P x V A operand (k index 8g + e is
+// key 4g + e for e < 4, then 16 + 4g + e - 4).
+template <int RS>
+__device__ __forceinline__ void prefill_weights(PrefillWave<RS>& w, const float (&x)[RS][2][4], uint4 (&pa)[RS][2],
+                                                float scale_log2) {
+#pragma unroll
+  for (int s = 0; s < RS; ++s) {
     const float neg_m = -w.m_ref[s];
     float p[2][4], rest[2][4];
 #pragma unroll
@@ -110,7 +145,7 @@ __device__ __forceinline__ void prefill_step(PrefillWave<RS>& w, const char* sta
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // a dropped key: exp2(-inf) = 0
-        p[tt][r] = __builtin_amdgcn_exp2f(fmaf(x[tt][r], scale_log2, neg_m));
+        p[tt][r] = __builtin_amdgcn_exp2f(fmaf(x[s][tt][r], scale_log2, neg_m));
         w.l_acc[s] += p[tt][r];
         rest[tt][r] = p[tt][r] - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p[tt][r]) & 0xffff0000u);
       }
@@ -122,19 +157,34 @@ __device__ __forceinline__ void prefill_step(PrefillWave<RS>& w, const char* sta
     pa[s][1] = make_uint4(lo2(rest[0][0], rest[0][1]), lo2(rest[0][2], rest[0][3]), lo2(rest[1][0], rest[1][1]),
                           lo2(rest[1][2], rest[1][3]));
   }
+}
 
-  // ---- O += P x V, 16 dims per product; each V operand serves every set and term ----
-  const char* vt = stage + kStageTile + (4 * g + (i >> 2)) * kStageRow + (i & 3) * 8;
+// O += P x V, 16 dims per product; each V operand serves every set and term.
+// The wave runs the products at raised priority: when both waves of a SIMD
+// are ready to issue, the products go first and the other wave's vector work
+// fills the cycles the matrix core leaves to the vector unit.
+template <int RS>
+__device__ __forceinline__ void prefill_pv(PrefillWave<RS>& w, const uint4 (&pa)[RS][2], const lds_char* stage,
+                                           int lane) {
+  __builtin_amdgcn_s_setprio(1);
+  const int i = lane & 15, g = lane >> 4;
+  // one address register per step; the empty asm keeps the compiler from
+  // hoisting a register per (j, half) out of the tile loop, so the offsets
+  // below stay immediate fields of the reads
+  uint32_t va = (uint32_t)(uintptr_t)(stage + kKTileBytes + (4 * g + (i >> 2)) * kVRow + (i & 3) * 8);
+  asm volatile("" : "+v"(va));
+  const lds_char* vt = (const lds_char*)(uintptr_t)va;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint2 v0 = lds_read_tr16(vt + j * 32);
-    const uint2 v1 = lds_read_tr16(vt + 16 * kStageRow + j * 32);
+    const uint2 v0 = lds_tr16_at(vt + j * 32);
+    const uint2 v1 = lds_tr16_at(vt + 16 * kVRow + j * 32);
     const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
     for (int s = 0; s < RS; ++s)
 #pragma unroll
       for (int e = 0; e < 2; ++e) w.o[s][j] = mfma_bf16(pa[s][e], vb, w.o[s][j]);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillParams p) {
@@ -186,12 +236,13 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
       vr[j] = rsrc_ld16(V, off + j * 16 * kRowBytes);
     }
   };
-  auto store_tile = [&](char* stage) {
-    char* q = stage + (t / 16) * kStageRow + (t % 16) * 16;
+  auto store_tile = [&](lds_char* stage) {
+    lds_char* qk = stage + (t / 16) * kKRow + (t % 16) * 16;
+    lds_char* qv = stage + kKTileBytes + (t / 16) * kVRow + (t % 16) * 16;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<uint4*>(q + j * 16 * kStageRow) = kr[j];
-      *reinterpret_cast<uint4*>(q + kStageTile + j * 16 * kStageRow) = vr[j];
+      *reinterpret_cast<lds_u32x4*>(qk + j * 16 * kKRow) = __builtin_bit_cast(u32x4_t, kr[j]);
+      *reinterpret_cast<lds_u32x4*>(qv + j * 16 * kVRow) = __builtin_bit_cast(u32x4_t, vr[j]);
     }
   };
 
@@ -203,18 +254,46 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
     aw.m_ref[s] = -INFINITY;
     aw.l_acc[s] = 0.f;
   }
-  if (ntiles > 0) load_tile(0);
+  // Tile t sits in stage t % 3. In iteration t the wave applies the softmax of
+  // tile t and multiplies it into O while its scores for tile t + 1 are
+  // computed (independent work for the matrix cores during the vector part);
+  // before the barrier the workgroup stores tile t + 1, after it loads tile
+  // t + 2 into registers. A stage is rewritten two barriers after its last read.
+  const int my_tiles = (wave_keys + kStepKeys - 1) / kStepKeys;  // tiles this wave multiplies
+  const int full_tiles = wave_first_keys / kStepKeys;            // ... without a masked key
+  lds_char* const lds = (lds_char*)smem;
+  auto stage_of = [&](int tile) { return lds + (tile % kPrefillStages) * kPStageBytes; };
+  f32x4_t sc[kRowSets][2];
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(stage_of(0));
+  }
+  if (ntiles > 1) load_tile(1);
+  __syncthreads();
+  if (my_tiles > 0) prefill_scores<kRowSets>(sc, stage_of(0), qb, lane);
   for (int tile = 0; tile < ntiles; ++tile) {
-    char* stage = smem + (tile & 1) * kStageBytes;
-    // the stage was last read two tiles ago, before the previous barrier
-    store_tile(stage);
+    if (tile + 1 < ntiles) store_tile(stage_of(tile + 1));
     __syncthreads();
-    if (tile + 1 < ntiles) load_tile(tile + 1);
+    if (tile + 2 < ntiles) load_tile(tile + 2);
+    if (tile >= my_tiles) continue;
     const int key0 = tile * kStepKeys;
-    if (key0 + kStepKeys <= wave_first_keys)
-      prefill_step<kRowSets, false>(aw, stage, qb, key0, end, p.scale_log2, lane);
-    else if (key0 < wave_keys)
-      prefill_step<kRowSets, true>(aw, stage, qb, key0, end, p.scale_log2, lane);
+    const bool next = tile + 1 < my_tiles;
+    float x[kRowSets][2][4];
+    uint4 pa[kRowSets][2];
+    if (tile < full_tiles && next) {
+      prefill_reference<kRowSets, false>(aw, sc, x, key0, end, p.scale_log2, lane);
+      prefill_scores<kRowSets>(sc, stage_of(tile + 1), qb, lane);
+      prefill_weights<kRowSets>(aw, x, pa, p.scale_log2);
+      prefill_pv<kRowSets>(aw, pa, stage_of(tile), lane);
+    } else {
+      if (tile < full_tiles)
+        prefill_reference<kRowSets, false>(aw, sc, x, key0, end, p.scale_log2, lane);
+      else
+        prefill_reference<kRowSets, true>(aw, sc, x, key0, end, p.scale_log2, lane);
+      prefill_weights<kRowSets>(aw, x, pa, p.scale_log2);
+      prefill_pv<kRowSets>(aw, pa, stage_of(tile), lane);
+      if (next) prefill_scores<kRowSets>(sc, stage_of(tile + 1), qb, lane);
+    }
   }
 
   // ---- normalise and store: element r of o[s][j] is row 16s + 4*grp + r, dim 16j + i ----
