@@ -221,10 +221,18 @@ int gemm_f16(const void* a_dev, const void* b_dev, void* c_dev, int32_t M, int32
  *  k_cache_dev   bf16 [B, Hkv, Lmax, D]
  *  v_cache_dev   bf16 [B, Hkv, Lmax, D]
  *  ctx_lens_dev  int32 [B], each in [T, Lmax] (precondition, not checked on the
- *                device; a value outside it gives undefined results)
+ *                device: the kernel clamps it to [0, Lmax] and reads no cache
+ *                row at or past it, but a token left with no key gets an
+ *                unspecified output)
  *  out_dev       bf16 [B, T, Hq*D], head-major within a token as in decode
- * head_dim 128 only; softmax_scale 0 selects 1/sqrt(head_dim). No workspace.
- * Returns DA_OK or a DA_ERR_* code (checks before any HIP call).
+ * head_dim 128 only, Hq a multiple of Hkv with Hq/Hkv <= DA_MAX_GROUP,
+ * 1 <= T <= Lmax, Lmax*D*2 < 4 GiB; softmax_scale 0 selects 1/sqrt(head_dim).
+ * Tensors: 16-byte aligned device pointers (ctx_lens 4-byte), owned by the
+ * caller; the library allocates nothing, needs no workspace and keeps no
+ * pointer after the call. The work is enqueued on `stream` (a hipStream_t,
+ * NULL = the default stream); outputs are valid once the caller synchronises.
+ * Returns DA_OK, DA_ERR_NULL, DA_ERR_ALIGN or DA_ERR_SHAPE before any HIP
+ * call, or DA_ERR_LAUNCH if the launch fails.
  */
 typedef struct {
   int32_t batch;
