@@ -261,3 +261,29 @@ def test_head_dim_256_plans_two_launches(lib):
     # the attention partials and the bf16 attention output are twice as wide as at 128
     narrow = da.decode_attn_workspace_size(da.make_shape(head_dim=128, flags=da.DA_FLAG_SEPARATE, **cfg))
     assert plan.workspace_bytes > narrow
+
+
+def _pre(lib, q=FAKE, k=FAKE, v=FAKE, cl=FAKE, out=FAKE, **kw):
+    fields = dict(batch=2, num_tokens=16, num_q_heads=32, num_kv_heads=8, head_dim=128, max_seq_len=1024,
+                  softmax_scale=0.0)
+    fields.update(kw)
+    s = da.PrefillAttnShape(**fields)
+    return lib.prefill_attn_fwd(q, k, v, cl, out, ctypes.byref(s), None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "cl", "out"])
+def test_prefill_null_pointers_are_rejected(lib, which):
+    assert _pre(lib, **{which: None}) == da.DA_ERR_NULL
+    assert lib.prefill_attn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == da.DA_ERR_NULL
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "out"])
+def test_prefill_misaligned_pointers_are_rejected(lib, which):
+    assert _pre(lib, **{which: FAKE + 2}) == da.DA_ERR_ALIGN
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim=256), dict(head_dim=64), dict(num_q_heads=30), dict(batch=0),
+                                dict(num_tokens=0), dict(num_tokens=2048), dict(num_kv_heads=1, num_q_heads=32),
+                                dict(max_seq_len=1 << 24)])
+def test_prefill_bad_shapes_are_rejected(lib, kw):
+    assert _pre(lib, **kw) == da.DA_ERR_SHAPE
