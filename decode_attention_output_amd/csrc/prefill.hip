@@ -37,20 +37,37 @@ constexpr int kPrefillWaves = 4;
 constexpr int kPrefillThreads = kPrefillWaves * kWave;
 constexpr int kRowSets = 2;                                // 16-row sets per wave
 constexpr int kPrefillRows = kPrefillWaves * 16 * kRowSets;  // query rows per workgroup
-constexpr int kPrefillStages = 3;                          // K/V stages shared by the waves
-// A stage holds a 32-key K tile and V tile. K rows are read 16 bytes a lane,
-// 16 rows per 16 lanes: a 272-byte row stride puts the rows on distinct banks.
-// V rows are read by transposing 8-byte reads, 4 rows x 32 bytes per 16
-// lanes: a 288-byte stride spreads those rows over the banks.
-constexpr int kKRow = kRowBytes + 16;
-constexpr int kVRow = kRowBytes + 32;
-constexpr int kKTileBytes = kStepKeys * kKRow;
-constexpr int kPStageBytes = kKTileBytes + kStepKeys * kVRow;
+constexpr int kPrefillStages = 4;                          // K/V stages shared by the waves
+// A stage holds a 32-key K tile and V tile, 8 KiB each, written straight from
+// global memory by 16-byte LDS-direct loads (1 KiB per wave instruction, lane
+// l filling bytes 16l..16l+15), so the layout is any arrangement of the
+// tiles' 16-byte chunks. Chunk c (dims 8c..8c+7) of key row r sits at
+//   K: 512 c + 16 r                  (all 32 rows of a chunk together)
+//   V: 1024 (c / 2) + 32 r + 16 (c % 2)   (all 32 rows of a 16-dim block together)
+// With these, the K operand reads (16 rows x 16 bytes per 16 lanes) and the
+// transposing V reads (4 rows x 32 bytes per 16 lanes) cover contiguous bytes,
+// free of bank conflicts, and every read of a step is one per-lane base plus
+// an immediate offset.
+constexpr int kKTileBytes = kStepKeys * kRowBytes;
+constexpr int kPStageBytes = 2 * kKTileBytes;
 constexpr int kPrefillLds = kPrefillStages * kPStageBytes;
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+
+// One 16-byte LDS-direct load per lane: lane l's 16 bytes at `voff` of the
+// buffer land in LDS at `lds_addr` + 16 l. Issued as assembly so that the
+// compiler, which cannot tell the stages apart, does not wait for every such
+// load before each LDS read; the caller waits for the loads it needs (vmcnt)
+// and publishes them with a barrier. M0 is written here and used by nothing
+// else in the kernel; one wait state separates the M0 write from the load.
+__device__ __forceinline__ void lds_direct16(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
 
 // Transposing LDS read of four 16-bit elements at an LDS address.
 __device__ __forceinline__ uint2 lds_tr16_at(const lds_char* p) {
@@ -79,12 +96,16 @@ __device__ __forceinline__ void prefill_scores(f32x4_t (&sc)[RS][2], const lds_c
   for (int s = 0; s < RS; ++s)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) sc[s][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // row 16 tt + i, chunk 4 kk + g: base 512 g + 16 i, offset 2048 kk + 256 tt; the
+  // empty asm keeps the base one register so the offsets stay immediate
+  uint32_t ka = 512 * g + 16 * i;
+  asm volatile("" : "+v"(ka));
+  const lds_char* kb = stage + ka;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const lds_char* kr = stage + (16 * tt + i) * kKRow + g * 16;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint4 a = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(kr + kk * 64));
+      const uint4 a = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(kb + 2048 * kk + 256 * tt));
 #pragma unroll
       for (int s = 0; s < RS; ++s) sc[s][tt] = mfma_bf16(a, qb[s][kk], sc[s][tt]);
     }
@@ -168,16 +189,16 @@ __device__ __forceinline__ void prefill_pv(PrefillWave<RS>& w, const uint4 (&pa)
                                            int lane) {
   __builtin_amdgcn_s_setprio(1);
   const int i = lane & 15, g = lane >> 4;
-  // one address register per step; the empty asm keeps the compiler from
-  // hoisting a register per (j, half) out of the tile loop, so the offsets
-  // below stay immediate fields of the reads
-  uint32_t va = (uint32_t)(uintptr_t)(stage + kKTileBytes + (4 * g + (i >> 2)) * kVRow + (i & 3) * 8);
+  // lane (i, g) reads 8 bytes of row 4 g + i / 4 (+ 16 for the second half) at
+  // byte 8 (i % 4) of the block's 32: base 8 lane, offset 1024 j + 512 half; one
+  // address register per step (the empty asm keeps the offsets immediate)
+  uint32_t va = kKTileBytes + 8 * lane;
   asm volatile("" : "+v"(va));
-  const lds_char* vt = (const lds_char*)(uintptr_t)va;
+  const lds_char* vt = stage + va;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint2 v0 = lds_tr16_at(vt + j * 32);
-    const uint2 v1 = lds_tr16_at(vt + 16 * kVRow + j * 32);
+    const uint2 v0 = lds_tr16_at(vt + 1024 * j);
+    const uint2 v1 = lds_tr16_at(vt + 1024 * j + 512);
     const uint4 vb = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
     for (int s = 0; s < RS; ++s)
@@ -204,17 +225,11 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
 
   // ---- this wave's rows: the queries (B operands) and the number of keys each row sees ----
   const int r0 = blk * kPrefillRows + wave * 16 * kRowSets;
-  uint4 qb[kRowSets][4];
   int end[kRowSets];
 #pragma unroll
   for (int s = 0; s < kRowSets; ++s) {
     const int rr = r0 + 16 * s + i;
-    const bool ok = rr < R;
-    const int tok = rr / p.G, gq = rr % p.G;
-    const uint16_t* qrow = p.q + (((size_t)b * p.T + tok) * p.Hq + (size_t)h * p.G + gq) * kHeadDim;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qb[s][kk] = ok ? ld16(qrow + kk * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
-    end[s] = ok ? base + tok + 1 : 1;             // keys 0 .. end-1 (a row past the end: key 0, not stored)
+    end[s] = rr < R ? base + rr / p.G + 1 : 1;  // keys 0 .. end-1 (a row past the end: key 0, not stored)
   }
   // keys of the wave's first and last rows, and of the workgroup's last row
   const int wave_first_keys = r0 < R ? base + r0 / p.G + 1 : 0;
@@ -226,24 +241,38 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   const rsrc_t K = make_rsrc(p.k + kv_off, (uint32_t)ctx * kRowBytes);  // rows past the context read as 0
   const rsrc_t V = make_rsrc(p.v + kv_off, (uint32_t)ctx * kRowBytes);
 
-  // ---- the shared K/V tiles: thread t loads rows t/16 and 16 + t/16, bytes (t%16)*16 ----
-  uint4 kr[2], vr[2];
-  auto load_tile = [&](int tile) {
-    const uint32_t off = (uint32_t)(tile * kStepKeys + t / 16) * kRowBytes + (t % 16) * 16;
+  lds_char* const lds = (lds_char*)smem;
+  auto stage_of = [&](int tile) { return lds + (tile % kPrefillStages) * kPStageBytes; };
+
+  // ---- the shared K/V tiles, loaded straight into LDS: wave w writes K blocks 2w, 2w + 1
+  // (chunks 2q, 2q + 1 of all 32 rows: lane l takes row l % 32, chunk 2q + l / 32) and V
+  // blocks 2w, 2w + 1 (dims 16j.. of all rows: lane l takes row l / 2, chunk 2j + l % 2) ----
+  uint32_t koff[2], voff[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      kr[j] = rsrc_ld16(K, off + j * 16 * kRowBytes);
-      vr[j] = rsrc_ld16(V, off + j * 16 * kRowBytes);
+  for (int u = 0; u < 2; ++u) {
+    const int q = 2 * wave + u;
+    koff[u] = (uint32_t)((lane & 31) * kRowBytes + (2 * q + (lane >> 5)) * 16);
+    voff[u] = (uint32_t)((lane >> 1) * kRowBytes + (2 * q + (lane & 1)) * 16);
+  }
+  auto issue_tile = [&](int tile) {  // 4 loads per wave
+    lds_char* stage = stage_of(tile);
+    const uint32_t t0 = (uint32_t)tile * kKTileBytes;
+    const uint32_t sa = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)stage + 2048 * wave);  // wave-uniform
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      lds_direct16(K, sa + 1024 * u, t0 + koff[u]);
+      lds_direct16(V, sa + kKTileBytes + 1024 * u, t0 + voff[u]);
     }
   };
-  auto store_tile = [&](lds_char* stage) {
-    lds_char* qk = stage + (t / 16) * kKRow + (t % 16) * 16;
-    lds_char* qv = stage + kKTileBytes + (t / 16) * kVRow + (t % 16) * 16;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *reinterpret_cast<lds_u32x4*>(qk + j * 16 * kKRow) = __builtin_bit_cast(u32x4_t, kr[j]);
-      *reinterpret_cast<lds_u32x4*>(qv + j * 16 * kVRow) = __builtin_bit_cast(u32x4_t, vr[j]);
-    }
+  // wait until this wave's loads of a tile are done while `newer` later tiles (4 loads
+  // each) stay in flight; the barrier after it makes the tile whole for every wave
+  auto wait_tile = [&](int newer) {
+    if (newer >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 8);  // vmcnt(8)
+    else if (newer == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 4);  // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
   };
 
   PrefillWave<kRowSets> aw;
@@ -261,20 +290,31 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
   // t + 2 into registers. A stage is rewritten two barriers after its last read.
   const int my_tiles = (wave_keys + kStepKeys - 1) / kStepKeys;  // tiles this wave multiplies
   const int full_tiles = wave_first_keys / kStepKeys;            // ... without a masked key
-  lds_char* const lds = (lds_char*)smem;
-  auto stage_of = [&](int tile) { return lds + (tile % kPrefillStages) * kPStageBytes; };
   f32x4_t sc[kRowSets][2];
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(stage_of(0));
+  // tiles 0, 1, 2 in flight; tile t + 3 is requested in step t, into the stage
+  // of tile t - 1, which every wave finished reading before step t's barrier
+#pragma unroll
+  for (int t0 = 0; t0 < 3; ++t0)
+    if (t0 < ntiles) issue_tile(t0);
+  // the queries (B operands), requested behind the first tiles; one full wait
+  // retires both before the loop (so that no wait inside it needs all loads)
+  uint4 qb[kRowSets][4];
+#pragma unroll
+  for (int s = 0; s < kRowSets; ++s) {
+    const int rr = r0 + 16 * s + i;
+    const int tok = rr / p.G, gq = rr % p.G;
+    const uint16_t* qrow = p.q + (((size_t)b * p.T + tok) * p.Hq + (size_t)h * p.G + gq) * kHeadDim;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[s][kk] = rr < R ? ld16(qrow + kk * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
   }
-  if (ntiles > 1) load_tile(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   if (my_tiles > 0) prefill_scores<kRowSets>(sc, stage_of(0), qb, lane);
   for (int tile = 0; tile < ntiles; ++tile) {
-    if (tile + 1 < ntiles) store_tile(stage_of(tile + 1));
+    // tile + 1 (read by this step) must be whole; tile + 2 may still be in flight
+    wait_tile(tile + 2 < ntiles ? 1 : 0);
     __syncthreads();
-    if (tile + 2 < ntiles) load_tile(tile + 2);
+    if (tile + 3 < ntiles) issue_tile(tile + 3);
     if (tile >= my_tiles) continue;
     const int key0 = tile * kStepKeys;
     const bool next = tile + 1 < my_tiles;
