@@ -283,16 +283,15 @@ __global__ __launch_bounds__(kPrefillThreads, 2) void prefill_kernel(PrefillPara
     aw.m_ref[s] = -INFINITY;
     aw.l_acc[s] = 0.f;
   }
-  // Tile t sits in stage t % 3. In iteration t the wave applies the softmax of
-  // tile t and multiplies it into O while its scores for tile t + 1 are
-  // computed (independent work for the matrix cores during the vector part);
-  // before the barrier the workgroup stores tile t + 1, after it loads tile
-  // t + 2 into registers. A stage is rewritten two barriers after its last read.
+  // Tile t sits in stage t % 4. In step t the wave turns tile t's scores into
+  // weights and multiplies them into O while its scores for tile t + 1 are
+  // computed (independent work for the matrix cores during the vector part).
+  // Before step t's barrier each wave waits for its own loads of tile t + 1;
+  // after it the workgroup requests tile t + 3 into the stage of tile t - 1,
+  // which every wave finished reading before that barrier.
   const int my_tiles = (wave_keys + kStepKeys - 1) / kStepKeys;  // tiles this wave multiplies
   const int full_tiles = wave_first_keys / kStepKeys;            // ... without a masked key
   f32x4_t sc[kRowSets][2];
-  // tiles 0, 1, 2 in flight; tile t + 3 is requested in step t, into the stage
-  // of tile t - 1, which every wave finished reading before step t's barrier
 #pragma unroll
   for (int t0 = 0; t0 < 3; ++t0)
     if (t0 < ntiles) issue_tile(t0);
