@@ -377,3 +377,15 @@ def test_prefill_of_one_token_matches_decode_attention(gpu):
     ref = oracle.attention(q[:, 0], k, v, cl)["ref"]
     assert_bf16_close(pre[:, 0], ref, "prefill T=1")
     assert_bf16_close(dec, ref, "decode")
+
+
+@pytest.mark.parametrize("wl", workloads.PREFILL, ids=lambda w: w.name)
+def test_prefill_benchmark_workloads(gpu, wl):
+    # the benchmarked sizes: every output of the first sequence (the whole prompt; one of the
+    # chunked sequences, each of which the kernel treats alike), against the oracle
+    inp = workloads.prefill_inputs(wl, poison=True)
+    out = host_words(da.prefill_attn_fwd(dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"]),
+                                         dev_i32(inp["ctx_lens"])))
+    ref = oracle.prefill_attention(inp["q"][:1], inp["k"][:1], inp["v"][:1], inp["ctx_lens"][:1])["ref"]
+    assert_bf16_close(out[:1], ref, wl.name)
+    assert np.all(np.isfinite(bf16_words_to_f64(out)))
