@@ -92,16 +92,19 @@ constexpr int kStepKeys = 32;  // keys per wave step
 // instruction of a wave reads 1 KiB, i.e. kRowsPerLoad whole rows, and a lane
 // holds kLoads 16-byte pieces of a 32-key K (or V) tile: piece c is row
 // kRowsPerLoad*c + lane/kLanesPerRow, bytes (lane%kLanesPerRow)*16. In LDS
-// every row is padded by 16 bytes (consecutive rows 4 banks apart).
+// the K rows are padded by 16 bytes (the 16-byte operand reads of 16 rows by
+// 16 lanes fall on distinct banks) and the V rows by 32 bytes (the
+// transposing reads of 4 rows x 32 bytes by 16 lanes fall on distinct banks).
 template <int HD>
 struct Dims {
   static constexpr int kRowBytes = HD * 2;
   static constexpr int kLanesPerRow = kRowBytes / 16;
   static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
   static constexpr int kLoads = kStepKeys / kRowsPerLoad;
-  static constexpr int kStageRow = kRowBytes + 16;
-  static constexpr int kStageTile = kStepKeys * kStageRow;  // one 32-key K or V tile
-  static constexpr int kStageBytes = 2 * kStageTile;        // LDS of one wave: K tile, V tile
+  static constexpr int kStageRow = kRowBytes + 16;          // K row
+  static constexpr int kStageTile = kStepKeys * kStageRow;  // the 32-key K tile; the V tile follows
+  static constexpr int kStageRowV = kRowBytes + 32;         // V row
+  static constexpr int kStageBytes = kStageTile + kStepKeys * kStageRowV;  // LDS of one wave
 };
 constexpr int kStageRow = Dims<kHeadDim>::kStageRow;
 constexpr int kStageTile = Dims<kHeadDim>::kStageTile;
@@ -148,11 +151,11 @@ template <int HD = kHeadDim>
 __device__ __forceinline__ void stage_kv(char* stage, const KVTileT<HD>& t, int lane) {
   using Dm = Dims<HD>;
   char* p = stage + (lane / Dm::kLanesPerRow) * Dm::kStageRow + (lane % Dm::kLanesPerRow) * 16;
+  char* pv = stage + Dm::kStageTile + (lane / Dm::kLanesPerRow) * Dm::kStageRowV + (lane % Dm::kLanesPerRow) * 16;
 #pragma unroll
   for (int c = 0; c < Dm::kLoads; ++c) *reinterpret_cast<uint4*>(p + c * Dm::kRowsPerLoad * Dm::kStageRow) = t.k[c];
 #pragma unroll
-  for (int c = 0; c < Dm::kLoads; ++c)
-    *reinterpret_cast<uint4*>(p + Dm::kStageTile + c * Dm::kRowsPerLoad * Dm::kStageRow) = t.v[c];
+  for (int c = 0; c < Dm::kLoads; ++c) *reinterpret_cast<uint4*>(pv + c * Dm::kRowsPerLoad * Dm::kStageRowV) = t.v[c];
 }
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -163,6 +166,14 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
   const bf16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
       (lds_bf16x4_t*)(__attribute__((address_space(3))) char*)(const_cast<char*>(p)));
   return __builtin_bit_cast(uint2, r);
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Transposing LDS read of four 16-bit elements at an LDS address (offsets added
+// to an LDS-space pointer fold into the instruction's offset field).
+__device__ __forceinline__ uint2 lds_tr16_at(const lds_char* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)const_cast<lds_char*>(p)));
 }
 
 // bf16 pair of two floats whose low 16 bits are zero: the high halves.
@@ -208,17 +219,18 @@ __device__ __forceinline__ void attn_step(AttnWaveT<HD>& w, const char* stage, c
       }
   }
 
-  // ---- online softmax with lazy rescale ----
-  float mx = s2[0][0];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s2[tt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  if (__builtin_amdgcn_ballot_w64(mx > w.m_ref + kRescaleSlack) != 0) {
+  // ---- online softmax with lazy rescale: the reference moves only when some
+  // lane's own scores pass it by the slack; only then is the row max over the
+  // four lanes of a row taken ----
+  const float lmx = fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), s2[0][2]), s2[0][3]), s2[1][0]),
+                                      s2[1][1]),
+                                s2[1][2]),
+                          s2[1][3]);
+  if (__builtin_amdgcn_ballot_w64(lmx > w.m_ref + kRescaleSlack) != 0) {
+    float mx = fmaxf(lmx, __shfl_xor(lmx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mn = fmaxf(w.m_ref, mx);
-    const float alpha = w.m_ref == -INFINITY ? 0.f : exp2f(w.m_ref - mn);
+    const float alpha = w.m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(w.m_ref - mn);
     w.m_ref = mn;
     w.l_acc *= alpha;
     // accumulator row 4g + r belongs to query 4g + r, whose factor lane 4g + r holds
@@ -236,7 +248,7 @@ __device__ __forceinline__ void attn_step(AttnWaveT<HD>& w, const char* stage, c
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       // a masked key has weight 0 (also while the reference max is still -inf)
-      p[tt][r] = s2[tt][r] > -INFINITY ? exp2f(s2[tt][r] - w.m_ref) : 0.f;
+      p[tt][r] = s2[tt][r] > -INFINITY ? __builtin_amdgcn_exp2f(s2[tt][r] - w.m_ref) : 0.f;
       w.l_acc += p[tt][r];
     }
 
@@ -259,14 +271,19 @@ __device__ __forceinline__ void attn_step(AttnWaveT<HD>& w, const char* stage, c
   const uint4 a_hi = pack(hi), a_mid = pack(mid), a_lo = pack(lo);
 
   // ---- O += P x V, 16 dims per product, 128 dims at a time ----
+  // one LDS address register per step; the empty asm keeps the compiler from
+  // holding a register per read across the loop, so the offsets stay immediate
+  uint32_t voff = Dm::kStageTile + (4 * g + (i >> 2)) * Dm::kStageRowV + (i & 3) * 8;
+  asm volatile("" : "+v"(voff));
+  const lds_char* vbase = (const lds_char*)stage + voff;
 #pragma unroll
   for (int h0 = 0; h0 < HD / 16; h0 += 8) {
-    const char* vt = stage + Dm::kStageTile + (4 * g + (i >> 2)) * Dm::kStageRow + (i & 3) * 8 + h0 * 32;
+    const lds_char* vt = vbase + h0 * 32;
     uint4 vb[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint2 v0 = lds_read_tr16(vt + j * 32);
-      const uint2 v1 = lds_read_tr16(vt + 16 * Dm::kStageRow + j * 32);
+      const uint2 v0 = lds_tr16_at(vt + j * 32);
+      const uint2 v1 = lds_tr16_at(vt + 16 * Dm::kStageRowV + j * 32);
       vb[j] = make_uint4(v0.x, v0.y, v1.x, v1.y);
     }
 #pragma unroll

@@ -52,7 +52,6 @@ constexpr int kKTileBytes = kStepKeys * kRowBytes;
 constexpr int kPStageBytes = 2 * kKTileBytes;
 constexpr int kPrefillLds = kPrefillStages * kPStageBytes;
 
-typedef __attribute__((address_space(3))) char lds_char;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
@@ -69,10 +68,6 @@ __device__ __forceinline__ void lds_direct16(rsrc_t r, uint32_t lds_addr, uint32
                : "memory", "m0");
 }
 
-// Transposing LDS read of four 16-bit elements at an LDS address.
-__device__ __forceinline__ uint2 lds_tr16_at(const lds_char* p) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)const_cast<lds_char*>(p)));
-}
 
 template <int RS>
 struct PrefillWave {
