@@ -80,8 +80,8 @@ bool tiles_ok(const decode_attn_shape_t* s) {
   if (t->proj_ksplit < 0 || t->step_mode < 0 || t->step_mode > 2) return false;
   if (const int tn = t->proj_tile_n) {
     if (tn != 64 && tn != 128 && tn != 256 && tn != 512) return false;
-    if (s->batch < 16 && pow2_at_least(s->batch) * tn > 2048) return false;
-    if (s->batch >= 16 && tn != da::kGemmTileN) return false;
+    // 128 is the MFMA GEMM's tile; the other widths ask for the GEMV (batch < 16)
+    if (tn != da::kGemmTileN && (s->batch >= 16 || pow2_at_least(s->batch) * tn > 2048)) return false;
   }
   return true;
 }
@@ -116,7 +116,12 @@ struct ProjPlan {
 // tile override, already range-checked by tiles_ok).
 ProjPlan plan_proj(int M, int K, int N, int tile_n_req = 0, int ksplit_req = 0) {
   ProjPlan pp{};
-  if (M < 16) {
+  // The MFMA GEMM streams the weight in 1 KiB row blocks per load instruction
+  // and was measured faster than the GEMV at every batch (1, 2, 4, 8; 2-9 %
+  // per step); the GEMV serves a K that is not a multiple of 32 and a tile
+  // width only it has (64, 256 or 512 columns, batch < 16).
+  const bool gemv = M < 16 && (K % 32 != 0 || (tile_n_req != 0 && tile_n_req != da::kGemmTileN));
+  if (gemv) {
     // GEMV: column tiles of up to 256 columns (512 bytes of each weight row
     // per workgroup) and a K-chunk sized so that about kTargetProjWorkgroups
     // workgroups stream the weight; every lane keeps 8 rows in flight.

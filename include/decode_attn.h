@@ -72,11 +72,13 @@ extern "C" {
  *  attn_depth       32-key steps each attention wave has in flight while it
  *                   computes one, 1..3 (1 only at head_dim 256)
  *  proj_tile_n      output columns per projection workgroup: 64, 128, 256 or
- *                   512 (the GEMV for B < 16 also needs tile_n * B <= 2048 after
- *                   B is rounded up to a power of two; the MFMA GEMM for
- *                   B >= 16 takes 128 only; the single-launch step takes 128,
- *                   256 or 512 and falls back to two launches if the shape
- *                   does not fit that tile)
+ *                   512. 128 is the MFMA GEMM's tile (the built-in projection
+ *                   of the two-launch step at every batch); 64, 256 and 512
+ *                   select the VALU GEMV instead, for B < 16 only, with
+ *                   tile_n * B <= 2048 after B is rounded up to a power of two.
+ *                   The single-launch step takes 128, 256 or 512 for its own
+ *                   projection and falls back to two launches if the shape
+ *                   does not fit that tile
  *  proj_ksplit      K-chunks the projection is cut into, >= 1 (rounded so that
  *                   every chunk is a whole number of the kernel's row batches)
  *  step_mode        0 built-in, 1 one launch where the single-launch step
@@ -153,7 +155,7 @@ typedef struct {
   decode_attn_matmul_plan_t oproj;  /* attn_output_flat x o_weight: M=B, K=Hq*D, N   */
   int32_t split_len;    /* keys per attention workgroup (flash-decoding split)       */
   int32_t num_splits;   /* ceil(max_seq_len / split_len)                              */
-  int32_t oproj_path;   /* 0: VALU GEMV (B < 16), 1: MFMA GEMM (B >= 16)             */
+  int32_t oproj_path;   /* 0: VALU GEMV, 1: MFMA GEMM (two-launch projection)        */
   int32_t fused;        /* 1: decode_attn_fwd runs the step as one launch (small
                            steps, B < 16): projection workgroups stream their weight
                            tile while the attention runs, then wait for it          */
@@ -194,7 +196,8 @@ size_t oproj_workspace_size(int32_t M, int32_t K, int32_t N);
 /*
  * The output projection alone (the third matmul of the F-16 page):
  * out[M,N] = x[M,K] @ w[K,N]; bf16 in, fp32 accumulation, bf16 out (round to
- * nearest even). M < 16 runs a VALU GEMV, M >= 16 an MFMA GEMM. `workspace`
+ * nearest even). It runs an MFMA GEMM (K a multiple of 32 for every M) or,
+ * for M < 16 with K a multiple of 8 only, a VALU GEMV. `workspace`
  * (>= oproj_workspace_size bytes, zero-filled before first use, may be NULL
  * when that size is 0) holds split-K partial sums and counters.
  */

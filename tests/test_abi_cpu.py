@@ -156,8 +156,9 @@ def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
         assert plan.qk.workgroups >= min(192, keys // 128)
         assert plan.split_len >= min(128, 32 * (-(-keys // 32)))
         assert plan.oproj.workgroups >= min(256, (cfg["hidden"] // 128) * (cfg["num_q_heads"] * 128 // 128))
-    # projection path: VALU GEMV below 16 rows, MFMA from 16 rows
-    assert plan.oproj_path == (1 if cfg["batch"] >= 16 else 0)
+    # projection path: the single-launch step's own VALU projection, else the MFMA GEMM at
+    # every batch (K = Hq*128)
+    assert plan.oproj_path == (0 if plan.fused else 1)
     assert plan.workspace_bytes == da.decode_attn_workspace_size(da.make_shape(**cfg))
 
 
@@ -193,6 +194,13 @@ def test_tile_override_out_of_range_is_a_shape_error(lib, tiles):
     assert _fwd(lib, shape) == da.DA_ERR_SHAPE
     with pytest.raises(da.DecodeAttnError):
         da.decode_attn_plan(shape)
+
+
+def test_gemv_is_chosen_by_its_own_widths(lib):
+    cfg = dict(batch=4, num_q_heads=64, num_kv_heads=8, max_seq_len=32768, hidden=8192)
+    for tn, path in ((0, 1), (128, 1), (64, 0), (256, 0), (512, 0)):
+        plan = da.decode_attn_plan(da.make_shape(tiles=dict(proj_tile_n=tn), **cfg))
+        assert plan.oproj_path == path and (tn == 0 or plan.oproj.tile_n == tn), tn
 
 
 def test_tile_override_gemv_width_limit(lib):
