@@ -219,10 +219,12 @@ def test_tile_override_reaches_the_plan(lib):
     assert over.num_splits == 320 and over.split_len * 320 >= 4 * 8 * 32768
     assert over.oproj.tile_n == 128 and over.oproj.split == 8
     assert over.oproj.workgroups == (8192 // 128) * 8
-    # zero fields keep the built-in choice
-    same = da.decode_attn_plan(da.make_shape(tiles={}, **cfg))
-    assert (same.qk.workgroups, same.oproj.tile_n, same.oproj.split) == (base.qk.workgroups, base.oproj.tile_n,
-                                                                         base.oproj.split)
+    # zero fields keep the built-in choice (a shape without a row in the measured table)
+    cfg2 = dict(cfg, max_seq_len=30000)
+    base2 = da.decode_attn_plan(da.make_shape(**cfg2))
+    same = da.decode_attn_plan(da.make_shape(tiles={}, **cfg2))
+    assert (same.qk.workgroups, same.oproj.tile_n, same.oproj.split) == (base2.qk.workgroups, base2.oproj.tile_n,
+                                                                         base2.oproj.split)
     # a grid wider than the blocks of the step is capped at one 32-key block per workgroup
     tiny = da.decode_attn_plan(da.make_shape(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=256, hidden=512,
                                              tiles=dict(attn_workgroups=1024, step_mode=2)))
