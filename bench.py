@@ -203,7 +203,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first (enough for the clock to settle: with 20 the first timed region ran ~9 %% slow)")
     ap.add_argument("--workload", default=workloads.PAGES.name,
                     choices=[w.name for w in workloads.DECODE + workloads.PREFILL])
     ap.add_argument("--min-rotate-mib", type=float, default=512.0)

@@ -348,6 +348,10 @@ PREFILL = [
     (2, 5, 2, 2, [33, 7], 40),
     (3, 33, 24, 8, [1000, 500, 33], 1024),
     (1, 256, 32, 8, [2048], 2048),
+    # small causal chunks (max_seq_len < 1.5 T, few row blocks): one row set per wave
+    (2, 100, 8, 2, [120, 100], 128),   # ragged prefix 20 and 0
+    (1, 300, 12, 4, [300], 310),       # 15 blocks of 64 rows, the last one partial
+    (1, 33, 4, 4, [33], 33),           # G = 1, one block
 ]
 
 
