@@ -9,11 +9,11 @@ namespace da {
 
 namespace {
 
-// head_dim 128: two workgroups fit a compute unit at one step in flight per
-// wave; deeper pipelines and head_dim 256 (whose K/V tile per step is twice
-// as large) use one workgroup per compute unit and its AGPRs.
+// One step in flight per wave: two workgroups fit a compute unit (head_dim 256
+// takes its steps in 16-key halves for that); deeper pipelines use one
+// workgroup per compute unit and its AGPRs.
 template <int GP, int NW, int D, int HD>
-__global__ __launch_bounds__(NW* kWave, (D == 1 && HD == 128) ? 2 : 1) void attn_streamk_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW* kWave, D == 1 ? 2 : 1) void attn_streamk_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_streamk_lds<NW, HD>()];
   attn_streamk_body<GP, NW, D, HD>(p, blockIdx.x, gridDim.x, smem);
 }

@@ -95,16 +95,21 @@ constexpr int kStepKeys = 32;  // keys per wave step
 // the K rows are padded by 16 bytes (the 16-byte operand reads of 16 rows by
 // 16 lanes fall on distinct banks) and the V rows by 32 bytes (the
 // transposing reads of 4 rows x 32 bytes by 16 lanes fall on distinct banks).
+// Above head_dim 128 a wave takes its 32-key steps as two 16-key halves (a
+// 16-row register set and stage), which keeps a lane's registers and a wave's
+// LDS small enough for two workgroups per compute unit.
 template <int HD>
 struct Dims {
   static constexpr int kRowBytes = HD * 2;
   static constexpr int kLanesPerRow = kRowBytes / 16;
   static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
   static constexpr int kLoads = kStepKeys / kRowsPerLoad;
-  static constexpr int kStageRow = kRowBytes + 16;          // K row
-  static constexpr int kStageTile = kStepKeys * kStageRow;  // the 32-key K tile; the V tile follows
-  static constexpr int kStageRowV = kRowBytes + 32;         // V row
-  static constexpr int kStageBytes = kStageTile + kStepKeys * kStageRowV;  // LDS of one wave
+  static constexpr bool kHalves = HD > 128;
+  static constexpr int kStageKeys = kHalves ? kStepKeys / 2 : kStepKeys;  // keys in a wave's stage
+  static constexpr int kStageRow = kRowBytes + 16;           // K row
+  static constexpr int kStageTile = kStageKeys * kStageRow;  // the K tile; the V tile follows
+  static constexpr int kStageRowV = kRowBytes + 32;          // V row
+  static constexpr int kStageBytes = kStageTile + kStageKeys * kStageRowV;  // LDS of one wave
 };
 constexpr int kStageRow = Dims<kHeadDim>::kStageRow;
 constexpr int kStageTile = Dims<kHeadDim>::kStageTile;
@@ -295,6 +300,114 @@ __device__ __forceinline__ void attn_step(AttnWaveT<HD>& w, const char* stage, c
   }
 }
 
+// ---- head_dim above 128: 16-key half steps ----
+template <int HD>
+struct KVHalfT {
+  uint4 k[Dims<HD>::kLoads / 2], v[Dims<HD>::kLoads / 2];  // 16 rows of K and of V
+};
+
+template <int HD>
+__device__ __forceinline__ void load_half(KVHalfT<HD>& t, const AttnSeg& sg, int key0, int lane) {
+  using Dm = Dims<HD>;
+  const uint32_t off = (uint32_t)(key0 + lane / Dm::kLanesPerRow) * Dm::kRowBytes + (lane % Dm::kLanesPerRow) * 16;
+#pragma unroll
+  for (int c = 0; c < Dm::kLoads / 2; ++c) t.k[c] = rsrc_ld16(sg.K, off + c * Dm::kRowsPerLoad * Dm::kRowBytes);
+#pragma unroll
+  for (int c = 0; c < Dm::kLoads / 2; ++c) t.v[c] = rsrc_ld16(sg.V, off + c * Dm::kRowsPerLoad * Dm::kRowBytes);
+}
+
+template <int HD>
+__device__ __forceinline__ void stage_half(char* stage, const KVHalfT<HD>& t, int lane) {
+  using Dm = Dims<HD>;
+  char* p = stage + (lane / Dm::kLanesPerRow) * Dm::kStageRow + (lane % Dm::kLanesPerRow) * 16;
+  char* pv = stage + Dm::kStageTile + (lane / Dm::kLanesPerRow) * Dm::kStageRowV + (lane % Dm::kLanesPerRow) * 16;
+#pragma unroll
+  for (int c = 0; c < Dm::kLoads / 2; ++c) *reinterpret_cast<uint4*>(p + c * Dm::kRowsPerLoad * Dm::kStageRow) = t.k[c];
+#pragma unroll
+  for (int c = 0; c < Dm::kLoads / 2; ++c)
+    *reinterpret_cast<uint4*>(pv + c * Dm::kRowsPerLoad * Dm::kStageRowV) = t.v[c];
+}
+
+// A 16-key half step starting at key0 on the 16-row K/V tile in the wave's
+// stage (keys >= end masked out): the 32-key step with keys 16..31 absent (zero
+// in both operands of P x V).
+template <int GP, int HD>
+__device__ __forceinline__ void attn_half_step(AttnWaveT<HD>& w, const char* stage, const uint4 (&qb)[HD / 32],
+                                               const AttnSeg& sg, int key0, int end, int lane) {
+  using Dm = Dims<HD>;
+  const int i = lane & 15, g = lane >> 4;
+  // ---- S^T = K x Q^T, one 16-key tile: lane (i, g) gets the scores of query i for keys 4g + r ----
+  f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const char* kr = stage + i * Dm::kStageRow + g * 16;
+#pragma unroll
+  for (int kk = 0; kk < HD / 32; ++kk) sc = mfma_bf16(*reinterpret_cast<const uint4*>(kr + kk * 64), qb[kk], sc);
+  float s2[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s2[r] = (key0 + 4 * g + r < end) ? sc[r] * sg.scale_log2 : -INFINITY;
+  if (sg.dbg && i < sg.G) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + 4 * g + r;
+      if (key < end) sg.dbg[(size_t)i * sg.dbg_stride + key] = sc[r] * sg.scale;
+    }
+  }
+  // ---- online softmax with lazy rescale (as in the 32-key step) ----
+  const float lmx = fmaxf(fmaxf(fmaxf(s2[0], s2[1]), s2[2]), s2[3]);
+  if (__builtin_amdgcn_ballot_w64(lmx > w.m_ref + kRescaleSlack) != 0) {
+    float mx = fmaxf(lmx, __shfl_xor(lmx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(w.m_ref, mx);
+    const float alpha = w.m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(w.m_ref - mn);
+    w.m_ref = mn;
+    w.l_acc *= alpha;
+    float ar[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
+#pragma unroll
+    for (int j = 0; j < HD / 16; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w.o[j][r] *= ar[r];
+  }
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p[r] = s2[r] > -INFINITY ? __builtin_amdgcn_exp2f(s2[r] - w.m_ref) : 0.f;
+    w.l_acc += p[r];
+  }
+  // three bf16 terms per weight; k index 8g + e is key 4g + e for e < 4, absent above
+  float hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    hi[r] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p[r]) & 0xffff0000u);
+    const float r1 = p[r] - hi[r];
+    mid[r] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, r1) & 0xffff0000u);
+    lo[r] = __builtin_bit_cast(float, bf16_bits_rne(r1 - mid[r]));
+  }
+  const uint4 a_hi = make_uint4(pack_hi(hi[0], hi[1]), pack_hi(hi[2], hi[3]), 0u, 0u);
+  const uint4 a_mid = make_uint4(pack_hi(mid[0], mid[1]), pack_hi(mid[2], mid[3]), 0u, 0u);
+  const uint4 a_lo = make_uint4(pack_hi(lo[0], lo[1]), pack_hi(lo[2], lo[3]), 0u, 0u);
+  // ---- O += P x V over the 16 rows, 16 dims per product ----
+  uint32_t voff = Dm::kStageTile + (4 * g + (i >> 2)) * Dm::kStageRowV + (i & 3) * 8;
+  asm volatile("" : "+v"(voff));
+  const lds_char* vbase = (const lds_char*)stage + voff;
+#pragma unroll
+  for (int h0 = 0; h0 < HD / 16; h0 += 8) {
+    const lds_char* vt = vbase + h0 * 32;
+    uint4 vb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint2 v0 = lds_tr16_at(vt + j * 32);
+      vb[j] = make_uint4(v0.x, v0.y, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w.o[h0 + j] = mfma_bf16(a_hi, vb[j], w.o[h0 + j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w.o[h0 + j] = mfma_bf16(a_mid, vb[j], w.o[h0 + j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w.o[h0 + j] = mfma_bf16(a_lo, vb[j], w.o[h0 + j]);
+  }
+}
+
 // The wave's steps first, first+step, ... (n of them, 32 keys each). D
 // register sets: a set is parked in LDS as its step begins and at once takes
 // the loads of the step D later, so D steps are in flight during a step.
@@ -302,6 +415,22 @@ template <int GP, int D, int HD = kHeadDim>
 __device__ __forceinline__ void attn_wave_steps(AttnWaveT<HD>& w, const uint4 (&qb)[HD / 32], const AttnSeg& sg,
                                                 int first, int step, int n, int end, char* stage, int lane) {
   if (n <= 0) return;
+  if constexpr (Dims<HD>::kHalves) {
+    // 2n half steps; one 16-row register set parked as its half begins
+    static_assert(D == 1, "one step in flight");
+    auto hkey = [&](int u) { return (first + (u >> 1) * step) * kStepKeys + (u & 1) * (kStepKeys / 2); };
+    KVHalfT<HD> t;
+    load_half<HD>(t, sg, hkey(0), lane);
+    for (int u = 0; u < 2 * n; ++u) {
+      wave_lds_fence();  // the previous half's LDS reads come first
+      stage_half<HD>(stage, t, lane);
+      if (u + 1 < 2 * n) load_half<HD>(t, sg, hkey(u + 1), lane);
+      wave_lds_fence();
+      attn_half_step<GP, HD>(w, stage, qb, sg, hkey(u), end, lane);
+    }
+    wave_lds_fence();
+    return;
+  }
   KVTileT<HD> t[D];
 #pragma unroll
   for (int j = 0; j < D; ++j)
