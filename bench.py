@@ -19,7 +19,12 @@ one buffer set (caches may serve it).
     python bench.py --workload prefill_b4_t512_h32kv8_ctx8192
 
 times the context (prefill) attention of a token chunk instead, in TFLOP/s
-against the bf16 MFMA peak.
+against the bf16 MFMA peak, and
+
+    python bench.py --workload gemm_f16_256x512x1024
+
+the dense fp16 GEMM check (integer-valued inputs, bit-exact against the
+oracle) against the fp16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ import argparse
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -41,6 +47,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
 PREFILL_METRIC = "TFLOP/s of context (prefill) attention of a token chunk vs bf16 MFMA peak, 1×MI355X"
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak of one MI355X
+GEMM_METRIC = "TFLOP/s of the dense fp16 GEMM check (MFMA, bit-exact) vs fp16 MFMA peak, 1×MI355X"
+SIMDS = 256 * 4  # SIMDs of one MI355X (256 compute units of 4)
+PEAK_CLOCK_GHZ = 2.4  # peak engine clock of one MI355X
 MALL_BYTES = 256 * 1024 * 1024
 
 
@@ -122,6 +132,126 @@ def prefill_alg_bytes(wl):
     return 2 * rows + 2 * 2 * wl.batch * wl.num_kv_heads * wl.ctx_len * wl.head_dim + 2 * rows
 
 
+def bench_gemm(args, wl):
+    """The dense fp16 GEMM check: C = A @ B with entries in {-1, 0, 1}, timed per launch."""
+    import numpy as np
+    import torch
+
+    import decode_attention_output_amd as da
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = da.load_library()
+    g = workloads.gemm_inputs(wl)
+    M, N, K = g["m"], g["n"], g["k"]
+    flops = 2 * M * N * K
+    set_bytes = 2 * (M * K + K * N + M * N)
+    R = max(1, math.ceil(args.min_rotate_mib * 2 ** 20 / set_bytes))
+
+    def to_dev(words):
+        return torch.from_numpy(np.ascontiguousarray(words).view(np.int16)).view(torch.float16).to(dev)
+
+    a0, b0 = to_dev(g["a"]), to_dev(g["b"])
+    stream = torch.cuda.Stream(device=dev)
+    sets = []
+    for r in range(R):
+        a, b = (a0, b0) if r == 0 else (a0.clone(), b0.clone())
+        c = torch.empty((M, N), dtype=torch.float16, device=dev)
+        sets.append((a, b, c))
+    handle = stream.cuda_stream
+
+    def launch(i):
+        a, b, c = sets[i % R]
+        rc = lib.gemm_f16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, handle)
+        if rc != da.DA_OK:
+            raise da.DecodeAttnError(rc, "gemm_f16")
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            launch(i)
+    torch.cuda.synchronize()
+
+    def run_steps(e0, e1, rotate):
+        e0.record(stream)
+        for i in range(args.steps):
+            launch(i if rotate else 0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gpu_ms = run_steps(ev0, ev1, True)
+    wall_us = (time.perf_counter() - t0) / args.steps * 1e6
+    gpu_us = gpu_ms * 1e3 / args.steps
+    repeats_us, median_us, warm_us = repeat_and_warm(run_steps, args.steps)
+    launch(0)
+    torch.cuda.synchronize()
+
+    achieved = flops / (gpu_us * 1e-6) / 1e12
+    result = {
+        "metric": GEMM_METRIC,
+        "value": round(achieved, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(gpu_us / 1e3, 6),
+        "us_per_step": round(gpu_us, 3),
+        "us_per_step_wall": round(wall_us, 3),
+        "us_per_step_repeats": repeats_us,
+        "us_per_step_median": median_us,
+        "us_per_step_warm": warm_us,
+        "warm_note": "one buffer set, so the Infinity Cache and L2 may serve it; value uses rotated sets",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "m": M, "n": N, "k": K, "flops": flops, "rotation_sets": R},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_kernel",
+            "achieved": round(achieved, 3),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 5),
+            "traffic": None,
+            "avg_launch_us": round(gpu_us, 3),
+            "flops_per_launch": flops,
+            "timing": "HIP events around the timed back-to-back launches on the bench stream",
+            "note": "0.27 GFLOP over 1.8 MB: a single launch is bound by latency, not by the matrix cores",
+        },
+    }
+    if not args.no_parity or not args.no_cpu_baseline:
+        import oracle
+
+        threads = oracle.default_threads()
+        n, t_cpu, ref = 0, 0.0, None
+        while n < 1 or (not args.no_cpu_baseline and t_cpu < args.cpu_seconds and n < 1000):
+            c0 = time.perf_counter()
+            ref, _ = oracle.gemm_f16(g["a"], g["b"], nthreads=threads)
+            t_cpu += time.perf_counter() - c0
+            n += 1
+    if not args.no_parity:
+        got = sets[0][2].cpu().view(torch.int16).numpy().view(np.uint16)
+        result["parity"] = {"vs": "oracle", "ok": bool(np.array_equal(got, ref)), "bit_exact": True,
+                            "mismatches": int(np.count_nonzero(got != ref))}
+    if not args.no_cpu_baseline:
+        cpu_us = t_cpu / n * 1e6
+        result["cpu_baseline"] = {
+            "value": round(flops / (cpu_us * 1e-6) / 1e12, 6),
+            "unit": "TFLOP/s",
+            "us_per_step": round(cpu_us, 1),
+            "cores": threads,
+            "kind": "oracle",
+            "sample": "%d runs of the %dx%dx%d GEMM (fp64 C oracle, %d threads, %.1f s)" % (n, M, N, K, threads, t_cpu),
+        }
+    print(json.dumps(result), flush=True)
+
+
 def summarize_profile(args):
     """profiles/<kernel>_<workload>.txt from a FETCH_SIZE run, a WRITE_SIZE run and a kernel-trace run."""
     import csv
@@ -197,6 +327,66 @@ def summarize_profile(args):
     print(out)
 
 
+def summarize_mfma(args):
+    """profiles/<kernel>_<workload>_mfma.txt: matrix-core counters of one kernel from a
+    --pmc run (SQ_INSTS_VALU_MFMA_MOPS_F16, SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) and a kernel-trace run."""
+    import csv
+
+    kname, pmc_csv, stats_csv = args.summarize_mfma
+    vals = {}
+    with open(pmc_csv) as f:
+        for row in csv.DictReader(f):
+            if kname in row.get("Kernel_Name", ""):
+                vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    avg = {c: sum(v) / len(v) for c, v in vals.items()}
+    full_name = None
+    stats = []
+    with open(stats_csv) as f:
+        for row in csv.DictReader(f):
+            stats.append((row["Name"], int(row["Calls"]), float(row["AverageNs"]), float(row["MinNs"]),
+                          float(row["MaxNs"])))
+            if kname in row["Name"] and full_name is None:
+                full_name = row["Name"]
+    trace_ns = next((a for n, _, a, _, _ in stats if kname in n), None)
+    mops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + avg.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+    # busy cycles are summed over the SIMDs; the kernel's own cycles come from its
+    # trace duration at the peak clock (GRBM_GUI_ACTIVE is summed over the 8 XCDs and
+    # spans the counter window around each dispatch, so it is only reported)
+    busy = avg.get("SQ_VALU_MFMA_BUSY_CYCLES")
+    util = 100.0 * busy / (trace_ns * PEAK_CLOCK_GHZ * SIMDS) if busy is not None and trace_ns else None
+    mfma_flops = mops * 512
+    stem = re.sub(r"[^A-Za-z0-9]+", "_", kname).strip("_")
+    out = os.path.join(PROFILES, "%s_%s_mfma.txt" % (stem, args.workload))
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(out, "w") as f:
+        f.write("# rocprofv3 matrix-core summary: %s, workload %s\n" % (kname, args.workload))
+        f.write("# commands (run from the repository root on one MI355X):\n")
+        f.write("#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph\n" % args.workload)
+        f.write("#   rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES "
+                "GRBM_GUI_ACTIVE --output-format csv -d <dir> -o mfma -- "
+                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph --steps 50\n" % args.workload)
+        f.write("#   python3 bench.py --workload %s --summarize-mfma '%s' <mfma csv> <stats csv>\n" % (args.workload, kname))
+        f.write("# matrix-core busy %% = SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (trace duration x %.1f GHz x %d "
+                "SIMDs)\n" % (PEAK_CLOCK_GHZ, SIMDS))
+        f.write("# executed matrix flops = (MOPS_F16 + MOPS_BF16) x 512, per dispatch\n")
+        f.write("# kernel trace (per kernel: calls, average / min / max ns):\n")
+        for name, calls, a, mn, mx in stats:
+            f.write("#   %-90s %6d %12.1f %12.1f %12.1f\n" % (name[:90], calls, a, mn, mx))
+        f.write("kernel = %s\n" % (full_name or kname))
+        f.write("source_hash = %s\n" % kernel_source_hash())
+        f.write("dispatches_counted = %d\n" % max((len(v) for v in vals.values()), default=0))
+        for c in sorted(avg):
+            f.write("%s_per_dispatch = %.1f\n" % (c, avg[c]))
+        f.write("mfma_flops_per_dispatch = %.0f\n" % mfma_flops)
+        f.write("mfma_busy_pct_at_peak_clock = %s\n" % (None if util is None else round(util, 3)))
+        f.write("trace_avg_ns = %s\n" % trace_ns)
+        if trace_ns:
+            f.write("executed_mfma_tflops = %.2f\n" % (mfma_flops / trace_ns / 1e3))
+    print(out)
+
+
 def parse():
     import workloads
 
@@ -206,7 +396,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=500,
                     help="untimed steps first (enough for the clock to settle: with 20 the first timed region ran ~9 %% slow)")
     ap.add_argument("--workload", default=workloads.PAGES.name,
-                    choices=[w.name for w in workloads.DECODE + workloads.PREFILL])
+                    choices=[w.name for w in workloads.DECODE + workloads.PREFILL + [workloads.GEMM]])
     ap.add_argument("--min-rotate-mib", type=float, default=512.0)
     ap.add_argument("--breakdown-steps", type=int, default=400, help="launches per kernel in the breakdown pass")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU oracle sample")
@@ -215,6 +405,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "TRACE_STATS_CSV"),
                     help="write the PMC/trace summary of a profiled run to profiles/ and exit")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("KERNEL", "PMC_CSV", "TRACE_STATS_CSV"),
+                    help="write the matrix-core counter summary of kernel KERNEL (a name prefix) in a profiled run "
+                         "of --workload to profiles/ and exit")
     return ap.parse_args()
 
 
@@ -222,6 +415,9 @@ def main():
     args = parse()
     if args.summarize_profile:
         summarize_profile(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -238,6 +434,9 @@ def main():
     wl = workloads.BY_NAME[args.workload]
     if isinstance(wl, workloads.PrefillWorkload):
         bench_prefill(args, wl)
+        return
+    if isinstance(wl, workloads.GemmWorkload):
+        bench_gemm(args, wl)
         return
     s = wl.shape
     dev = torch.device("cuda:0")

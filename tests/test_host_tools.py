@@ -54,3 +54,36 @@ def test_attention_only_workspace_covers_the_table_row():
     w = int(rows[0][len("TILE_ENTRY("):].split(",")[6])
     need_attn = da.decode_attn_workspace_size(da.make_shape(hidden=8, tiles=dict(attn_workgroups=w), **shape))
     assert da.decode_attn_workspace_size(da.make_shape(hidden=8, **shape)) >= need_attn
+
+
+def test_mfma_summary_from_counter_and_trace_csvs(tmp_path, monkeypatch):
+    # two dispatches of the counted kernel, one of another; busy % is the summed
+    # per-SIMD busy cycles over (trace duration x peak clock x SIMDs), flops are MOPS x 512
+    import bench
+
+    pmc = tmp_path / "mfma.csv"
+    rows = ["Kernel_Name,Counter_Name,Counter_Value"]
+    for kern in ("gemm_kernel<true, 1, 2>", "gemm_kernel<true, 1, 2>"):
+        rows += ["%s,SQ_INSTS_VALU_MFMA_MOPS_F16,524288" % kern.replace(",", ";"),
+                 "%s,SQ_VALU_MFMA_BUSY_CYCLES,102400" % kern.replace(",", ";"),
+                 "%s,GRBM_GUI_ACTIVE,1000" % kern.replace(",", ";")]
+    rows += ["other_kernel,SQ_INSTS_VALU_MFMA_MOPS_F16,7", "other_kernel,GRBM_GUI_ACTIVE,5"]
+    pmc.write_text("\n".join(rows) + "\n")
+    stats = tmp_path / "stats.csv"
+    stats.write_text("Name,Calls,AverageNs,MinNs,MaxNs\n"
+                     "gemm_kernel<true; 1; 2>,10,5000.0,4000.0,6000.0\nother_kernel,1,100.0,100.0,100.0\n")
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+
+    class A:
+        workload = "gemm_f16_256x512x1024"
+        summarize_mfma = ("gemm_kernel", str(pmc), str(stats))
+
+    bench.summarize_mfma(A())
+    text = (tmp_path / "profiles" / "gemm_kernel_gemm_f16_256x512x1024_mfma.txt").read_text()
+    assert "gemm_kernel<true; 1; 2>" in text
+    fields = dict(l.split(" = ", 1) for l in text.splitlines() if " = " in l and not l.startswith("#"))
+    assert fields["dispatches_counted"] == "2"
+    assert float(fields["mfma_flops_per_dispatch"]) == 524288 * 512
+    assert float(fields["mfma_busy_pct_at_peak_clock"]) == round(100.0 * 102400 / (5000.0 * 2.4 * 1024), 3)
+    assert float(fields["trace_avg_ns"]) == 5000.0
+    assert float(fields["executed_mfma_tflops"]) == round(524288 * 512 / 5000.0 / 1e3, 2)
