@@ -1,21 +1,24 @@
 // Output projection (the third matmul of one decode-attention forward in
 // "PyPTO 开箱性能调优实战：Decode Attention 多 Matmul 独立 TileShape 配置
-// F-16", section 代码对比: attn_output_flat x o_weight -> bf16) and the dense
-// MFMA GEMM used for M >= 16 and for the fp16 BasicMatmul check of the CANN
-// msKPP page "自动调优流程 / Kernel级自动调优".
+// F-16", section 代码对比: attn_output_flat x o_weight -> bf16) and the fp16
+// BasicMatmul check of the CANN msKPP page "自动调优流程 / Kernel级自动调优".
 //
-// M < 16 (a handful of decode tokens) is a skinny GEMV: every weight byte is
-// used M times, far below the MFMA ridge, so it runs on the vector ALUs.
-// A workgroup owns a tile of up to 512 output columns (1 KiB of each weight
-// row, read by one wave in one instruction) times a K-chunk of rows; every
-// lane keeps 8 rows of 16 bytes in flight. Partial sums of the K-chunks meet
-// in the workspace through device-coherent stores, and the last workgroup of
-// a column tile to arrive adds them in a fixed order (deterministic).
+// Both run on the MFMA GEMM below whenever K is a multiple of 32, at every M:
+// a projection of a few tokens is far below the MFMA ridge, so the weight
+// stream sets its pace, and the GEMM's whole-row-block loads stream it faster
+// than the GEMV (measured at M = 1, 2, 4 and 8). The weight tile is
+// transposed through LDS into the MFMA operand layout (B needs 8 consecutive
+// k per lane, the weight is row-major in n); the activation fragment is read
+// straight from global memory.
 //
-// M >= 16 is a real dense contraction and runs on MFMA 16x16x32: the weight
-// tile is transposed through LDS into the operand layout (B needs 8
-// consecutive k per lane, the weight is row-major in n), the activation
-// fragment is read straight from global memory.
+// The VALU GEMV (M < 16) serves a K that is not a multiple of 32 and the
+// column-tile widths only it has. A workgroup owns a tile of up to 512 output
+// columns (1 KiB of each weight row, read by one wave in one instruction)
+// times a K-chunk of rows; every lane keeps 8 rows of 16 bytes in flight.
+//
+// In both, the partial sums of the K-chunks meet in the workspace through
+// device-coherent stores, and the last workgroup of an output tile to arrive
+// adds them in a fixed order (deterministic).
 #include "gemv_core.hpp"
 
 namespace da {
