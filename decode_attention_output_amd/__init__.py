@@ -9,7 +9,12 @@ raises.
 The names mirror the C entry points: ``decode_attn_fwd``, ``decode_attn_only``,
 ``oproj_fwd``, ``gemm_f16``, ``decode_attn_workspace_size``,
 ``oproj_workspace_size``, ``decode_attn_plan``, ``decode_attn_status_str``,
-``prefill_attn_fwd``.
+``prefill_attn_fwd``, ``decode_attn_step_status``.
+
+Before any call reaches the library, the torch wrappers check that the
+tensors agree with each other (batch, heads, head_dim, cache length,
+projection sizes, output and debug buffers): the C ABI sees only pointers,
+so a mismatch would otherwise make the kernels run past an allocation.
 """
 from __future__ import annotations
 
@@ -26,6 +31,7 @@ DA_ERR_SHAPE = -2
 DA_ERR_ALIGN = -3
 DA_ERR_WORKSPACE = -4
 DA_ERR_LAUNCH = -5
+DA_ERR_TIMEOUT = -6
 DA_HEAD_DIM = 128
 DA_HEAD_DIM_WIDE = 256
 DA_MAX_GROUP = 16
@@ -42,13 +48,14 @@ EXPORTED = (
     "gemm_f16",
     "decode_attn_status_str",
     "prefill_attn_fwd",
+    "decode_attn_step_status",
 )
 
 
 class DecodeAttnTiles(ctypes.Structure):
     """Tile override of one call (decode_attn_tiles_t); zero fields keep the built-in choice."""
     _fields_ = [(n, ctypes.c_int32) for n in ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit",
-                                              "step_mode")]
+                                              "step_mode", "step_wait_polls")]
 
 
 def make_tiles(tiles) -> Optional[DecodeAttnTiles]:
@@ -141,6 +148,8 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_f16.argtypes = [vp, vp, vp, i32, i32, i32, vp]
     lib.prefill_attn_fwd.restype = ctypes.c_int
     lib.prefill_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(PrefillAttnShape), vp]
+    lib.decode_attn_step_status.restype = ctypes.c_int
+    lib.decode_attn_step_status.argtypes = [vp, sz, vp]
     lib.decode_attn_status_str.restype = ctypes.c_char_p
     lib.decode_attn_status_str.argtypes = [ctypes.c_int]
     _lib = lib
@@ -205,29 +214,139 @@ def _ptr(t) -> Optional[int]:
 
 def _check_dev(name, t, dtype):
     torch = _torch()
-    if t.device.type != "cuda":
-        raise ValueError("%s must be a device tensor" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     return torch
 
 
+def _dims(name, t, n):
+    if t.dim() != n:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, n, tuple(t.shape)))
+    return tuple(int(x) for x in t.shape)
+
+
+def _want(name, t, shape):
+    if tuple(int(x) for x in t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _same_device(*named):
+    devs = {(t.device.type, t.device.index) for _, t in named if t is not None}
+    if len(devs) > 1:
+        raise ValueError("tensors on different devices: %s" % ", ".join(
+            "%s on %s" % (n, t.device) for n, t in named if t is not None))
+
+
+def check_decode_tensors(q, k_cache, v_cache, seq_lens, o_weight=None, out=None, debug_scores=None,
+                         debug_lse=None):
+    """Shapes of one decode call's tensors against each other: q [B, Hq, D], K and V
+    [B, Hkv, Lmax, D] alike, seq_lens [B], o_weight [Hq*D, hidden], out [B, hidden] (or
+    [B, Hq*D] without o_weight), debug scores [B, Hq, Lmax] and lse [B, Hq] fp32.
+    Raises ValueError / TypeError; returns (B, Hq, Hkv, D, Lmax, hidden or 0)."""
+    B, Hq, D = _dims("q", q, 3)
+    Bk, Hkv, Lmax, Dk = _dims("k_cache", k_cache, 4)
+    if Bk != B or Dk != D:
+        raise ValueError("k_cache %s does not match q %s (batch and head_dim)" % (tuple(k_cache.shape),
+                                                                                 tuple(q.shape)))
+    _want("v_cache", v_cache, (Bk, Hkv, Lmax, Dk))
+    _want("seq_lens", seq_lens, (B,))
+    hidden = 0
+    if o_weight is not None:
+        Ko, hidden = _dims("o_weight", o_weight, 2)
+        if Ko != Hq * D:
+            raise ValueError("o_weight has %d rows, the projection's K is num_q_heads * head_dim = %d" % (Ko, Hq * D))
+    if out is not None:
+        _want("out", out, (B, hidden if o_weight is not None else Hq * D))
+    if (debug_scores is None) != (debug_lse is None):
+        raise ValueError("debug_scores and debug_lse go together")
+    if debug_scores is not None:
+        _want("debug_scores", debug_scores, (B, Hq, Lmax))
+        _want("debug_lse", debug_lse, (B, Hq))
+        torch = _torch()
+        for n, t in (("debug_scores", debug_scores), ("debug_lse", debug_lse)):
+            _check_dev(n, t, torch.float32)
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o_weight", o_weight), ("out", out)):
+        if t is not None:
+            _check_dev(n, t, torch.bfloat16)
+    _check_dev("seq_lens", seq_lens, torch.int32)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens),
+                 ("o_weight", o_weight), ("out", out), ("debug_scores", debug_scores), ("debug_lse", debug_lse))
+    return B, Hq, Hkv, D, Lmax, hidden
+
+
+def check_matmul_tensors(x, w, out=None, dtype=None):
+    """x [M, K], w [K, N], out [M, N], all of one 16-bit dtype on one device."""
+    M, K = _dims("x", x, 2)
+    Kw, N = _dims("w", w, 2)
+    if Kw != K:
+        raise ValueError("w has %d rows, x has %d columns" % (Kw, K))
+    if out is not None:
+        _want("out", out, (M, N))
+    torch = _torch()
+    dtype = dtype or torch.bfloat16
+    for n, t in (("x", x), ("w", w), ("out", out)):
+        if t is not None:
+            _check_dev(n, t, dtype)
+    _same_device(("x", x), ("w", w), ("out", out))
+    return M, K, N
+
+
+def check_prefill_tensors(q, k_cache, v_cache, ctx_lens, out=None):
+    """q [B, T, Hq, D], K and V [B, Hkv, Lmax, D], ctx_lens [B], out [B, T, Hq*D]."""
+    B, T, Hq, D = _dims("q", q, 4)
+    Bk, Hkv, Lmax, Dk = _dims("k_cache", k_cache, 4)
+    if Bk != B or Dk != D:
+        raise ValueError("k_cache %s does not match q %s (batch and head_dim)" % (tuple(k_cache.shape),
+                                                                                 tuple(q.shape)))
+    _want("v_cache", v_cache, (Bk, Hkv, Lmax, Dk))
+    _want("ctx_lens", ctx_lens, (B,))
+    if out is not None:
+        _want("out", out, (B, T, Hq * D))
+    torch = _torch()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+        if t is not None:
+            _check_dev(n, t, torch.bfloat16)
+    _check_dev("ctx_lens", ctx_lens, torch.int32)
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("ctx_lens", ctx_lens), ("out", out))
+    return B, T, Hq, Hkv, D, Lmax
+
+
 class Workspace:
-    """Zero-filled device scratch reused across calls (grows on demand)."""
+    """Zero-filled device scratch reused across calls (grows on demand). The
+    zero fill is enqueued on the stream of the call that needs it, so it is
+    ordered before that call's kernels."""
 
     def __init__(self, device=None):
         self.device = device
         self.buf = None
 
-    def get(self, nbytes: int):
+    def get(self, nbytes: int, stream=None):
         torch = _torch()
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device or "cuda")
+            s = stream if stream is not None else torch.cuda.current_stream(self.device)
+            with torch.cuda.stream(s):
+                self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device or "cuda")
         return self.buf
+
+
+def decode_attn_step_status(workspace, stream=None) -> int:
+    """DA_OK, or DA_ERR_TIMEOUT if a single-launch step on this workspace gave up
+    waiting since its counters were last zero-filled (waits for the stream)."""
+    buf = getattr(workspace, "buf", workspace)
+    if buf is None:
+        return DA_OK  # never used: no single-launch step ran on it
+    return int(load_library().decode_attn_step_status(buf.data_ptr(), buf.numel(), _stream_handle(stream)))
+
+
+def _ws_for(workspace, device, need, stream):
+    return (workspace or Workspace(device)).get(need, stream)
 
 
 def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Optional[Workspace] = None,
@@ -236,21 +355,16 @@ def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace
     """One decode step: returns out [B, hidden] bf16. ``separate`` asks for two
     launches (attention, projection) where the plan would use one; ``tiles``
     overrides the tile choice (decode_attn_tiles_t fields)."""
-    torch = _check_dev("q", q, _torch().bfloat16)
-    _check_dev("k_cache", k_cache, torch.bfloat16)
-    _check_dev("v_cache", v_cache, torch.bfloat16)
-    _check_dev("seq_lens", seq_lens, torch.int32)
-    _check_dev("o_weight", o_weight, torch.bfloat16)
-    B, Hq, D = q.shape
-    _, Hkv, Lmax, _ = k_cache.shape
-    hidden = o_weight.shape[1]
+    B, Hq, Hkv, D, Lmax, hidden = check_decode_tensors(q, k_cache, v_cache, seq_lens, o_weight, out, debug_scores,
+                                                       debug_lse)
+    torch = _torch()
     if out is None:
         out = torch.empty((B, hidden), dtype=torch.bfloat16, device=q.device)
     flags = (DA_FLAG_DEBUG_SCORES if debug_scores is not None else 0) | (DA_FLAG_SEPARATE if separate else 0)
     shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale, flags=flags, debug_scores=_ptr(debug_scores),
                        debug_lse=_ptr(debug_lse), tiles=tiles)
     need = decode_attn_workspace_size(shape)
-    ws = (workspace or Workspace(q.device)).get(need)
+    ws = _ws_for(workspace, q.device, need, stream)
     shape.workspace = _ptr(ws)
     shape.workspace_bytes = 0 if ws is None else ws.numel()
     rc = load_library().decode_attn_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
@@ -264,19 +378,16 @@ def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace
 def decode_attn_only(q, k_cache, v_cache, seq_lens, out=None, workspace: Optional[Workspace] = None,
                      softmax_scale: float = 0.0, debug_scores=None, debug_lse=None, stream=None, tiles=None):
     """Attention only: returns the bf16 [B, Hq*D] head-major attention output."""
-    torch = _check_dev("q", q, _torch().bfloat16)
-    _check_dev("k_cache", k_cache, torch.bfloat16)
-    _check_dev("v_cache", v_cache, torch.bfloat16)
-    _check_dev("seq_lens", seq_lens, torch.int32)
-    B, Hq, D = q.shape
-    _, Hkv, Lmax, _ = k_cache.shape
+    B, Hq, Hkv, D, Lmax, _ = check_decode_tensors(q, k_cache, v_cache, seq_lens, None, out, debug_scores,
+                                                  debug_lse)
+    torch = _torch()
     if out is None:
         out = torch.empty((B, Hq * D), dtype=torch.bfloat16, device=q.device)
     flags = DA_FLAG_DEBUG_SCORES if debug_scores is not None else 0
     shape = make_shape(B, Hq, Hkv, Lmax, 8, D, softmax_scale, flags=flags, debug_scores=_ptr(debug_scores),
                        debug_lse=_ptr(debug_lse), tiles=tiles)
     need = decode_attn_workspace_size(shape)
-    ws = (workspace or Workspace(q.device)).get(need)
+    ws = _ws_for(workspace, q.device, need, stream)
     shape.workspace = _ptr(ws)
     shape.workspace_bytes = 0 if ws is None else ws.numel()
     rc = load_library().decode_attn_only(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
@@ -288,14 +399,12 @@ def decode_attn_only(q, k_cache, v_cache, seq_lens, out=None, workspace: Optiona
 
 def oproj_fwd(x, w, out=None, workspace: Optional[Workspace] = None, stream=None):
     """out [M, N] = x [M, K] @ w [K, N], bf16."""
-    torch = _check_dev("x", x, _torch().bfloat16)
-    _check_dev("w", w, torch.bfloat16)
-    M, K = x.shape
-    N = w.shape[1]
+    M, K, N = check_matmul_tensors(x, w, out)
+    torch = _torch()
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     need = oproj_workspace_size(M, K, N)
-    ws = (workspace or Workspace(x.device)).get(need)
+    ws = _ws_for(workspace, x.device, need, stream)
     rc = load_library().oproj_fwd(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, K, N, _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream_handle(stream))
     if rc != DA_OK:
@@ -305,10 +414,8 @@ def oproj_fwd(x, w, out=None, workspace: Optional[Workspace] = None, stream=None
 
 def gemm_f16(a, b, c=None, stream=None):
     """C [M, N] = A [M, K] @ B [K, N], fp16."""
-    torch = _check_dev("a", a, _torch().float16)
-    _check_dev("b", b, torch.float16)
-    M, K = a.shape
-    N = b.shape[1]
+    torch = _torch()
+    M, K, N = check_matmul_tensors(a, b, c, dtype=torch.float16)
     if c is None:
         c = torch.empty((M, N), dtype=torch.float16, device=a.device)
     rc = load_library().gemm_f16(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, _stream_handle(stream))
@@ -320,12 +427,8 @@ def gemm_f16(a, b, c=None, stream=None):
 def prefill_attn_fwd(q, k_cache, v_cache, ctx_lens, out=None, softmax_scale: float = 0.0, stream=None):
     """Context attention of a chunk: q [B, T, Hq, D] -> out [B, T, Hq*D] bf16 (token t attends causally
     to keys 0 .. ctx_lens[b] - T + t)."""
-    torch = _check_dev("q", q, _torch().bfloat16)
-    _check_dev("k_cache", k_cache, torch.bfloat16)
-    _check_dev("v_cache", v_cache, torch.bfloat16)
-    _check_dev("ctx_lens", ctx_lens, torch.int32)
-    B, T, Hq, D = q.shape
-    _, Hkv, Lmax, _ = k_cache.shape
+    B, T, Hq, Hkv, D, Lmax = check_prefill_tensors(q, k_cache, v_cache, ctx_lens, out)
+    torch = _torch()
     if out is None:
         out = torch.empty((B, T, Hq * D), dtype=torch.bfloat16, device=q.device)
     shape = PrefillAttnShape(B, T, Hq, Hkv, D, Lmax, float(softmax_scale))
@@ -351,14 +454,14 @@ class PreparedCall:
         return self.result
 
 
-def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what, flags=0, tiles=None):
+def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what, flags=0, tiles=None, stream=None):
     B, Hq, D = q.shape
     _, Hkv, Lmax, _ = k_cache.shape
     shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale, flags=flags, tiles=tiles)
     need = decode_attn_workspace_size(shape)
     if need == 0:
         raise DecodeAttnError(DA_ERR_SHAPE, what)
-    ws = (workspace or Workspace(q.device)).get(need)
+    ws = _ws_for(workspace, q.device, need, stream)
     shape.workspace = _ptr(ws)
     shape.workspace_bytes = ws.numel()
     return shape, ws
@@ -367,14 +470,12 @@ def _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, what, flags=0, 
 def DecodeStep(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Optional[Workspace] = None,
                softmax_scale: float = 0.0, stream=None, separate=False, tiles=None) -> PreparedCall:
     """A prepared ``decode_attn_fwd``; calling it runs one decode step and returns ``out``."""
-    torch = _check_dev("q", q, _torch().bfloat16)
-    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("o_weight", o_weight)):
-        _check_dev(name, t, torch.bfloat16)
-    _check_dev("seq_lens", seq_lens, torch.int32)
+    B, _, _, _, _, hidden = check_decode_tensors(q, k_cache, v_cache, seq_lens, o_weight, out)
+    torch = _torch()
     if out is None:
-        out = torch.empty((q.shape[0], o_weight.shape[1]), dtype=torch.bfloat16, device=q.device)
-    shape, ws = _prepare_shape(q, k_cache, o_weight.shape[1], softmax_scale, workspace, "decode_attn_fwd",
-                               DA_FLAG_SEPARATE if separate else 0, tiles)
+        out = torch.empty((B, hidden), dtype=torch.bfloat16, device=q.device)
+    shape, ws = _prepare_shape(q, k_cache, hidden, softmax_scale, workspace, "decode_attn_fwd",
+                               DA_FLAG_SEPARATE if separate else 0, tiles, stream)
     tensors = (q, k_cache, v_cache, seq_lens, o_weight, out)
     args = [ctypes.c_void_p(t.data_ptr()) for t in tensors] + [ctypes.byref(shape),
                                                               ctypes.c_void_p(_stream_handle(stream))]
@@ -384,14 +485,12 @@ def DecodeStep(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace: Opt
 def AttentionStep(q, k_cache, v_cache, seq_lens, out=None, workspace: Optional[Workspace] = None,
                   softmax_scale: float = 0.0, stream=None, tiles=None) -> PreparedCall:
     """A prepared ``decode_attn_only``; calling it returns the bf16 [B, Hq*D] attention output."""
-    torch = _check_dev("q", q, _torch().bfloat16)
-    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        _check_dev(name, t, torch.bfloat16)
-    _check_dev("seq_lens", seq_lens, torch.int32)
-    B, Hq, D = q.shape
+    B, Hq, _, D, _, _ = check_decode_tensors(q, k_cache, v_cache, seq_lens, None, out)
+    torch = _torch()
     if out is None:
         out = torch.empty((B, Hq * D), dtype=torch.bfloat16, device=q.device)
-    shape, ws = _prepare_shape(q, k_cache, 8, softmax_scale, workspace, "decode_attn_only", tiles=tiles)
+    shape, ws = _prepare_shape(q, k_cache, 8, softmax_scale, workspace, "decode_attn_only", tiles=tiles,
+                               stream=stream)
     tensors = (q, k_cache, v_cache, seq_lens, out)
     args = [ctypes.c_void_p(t.data_ptr()) for t in tensors] + [ctypes.byref(shape),
                                                               ctypes.c_void_p(_stream_handle(stream))]
@@ -400,14 +499,12 @@ def AttentionStep(q, k_cache, v_cache, seq_lens, out=None, workspace: Optional[W
 
 def OprojStep(x, w, out=None, workspace: Optional[Workspace] = None, stream=None) -> PreparedCall:
     """A prepared ``oproj_fwd``; calling it returns out = x @ w (bf16)."""
-    torch = _check_dev("x", x, _torch().bfloat16)
-    _check_dev("w", w, torch.bfloat16)
-    M, K = x.shape
-    N = w.shape[1]
+    M, K, N = check_matmul_tensors(x, w, out)
+    torch = _torch()
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     need = oproj_workspace_size(M, K, N)
-    ws = (workspace or Workspace(x.device)).get(need)
+    ws = _ws_for(workspace, x.device, need, stream)
     args = [ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), ctypes.c_void_p(out.data_ptr()),
             ctypes.c_int32(M), ctypes.c_int32(K), ctypes.c_int32(N), ctypes.c_void_p(_ptr(ws)),
             ctypes.c_size_t(0 if ws is None else ws.numel()), ctypes.c_void_p(_stream_handle(stream))]

@@ -78,6 +78,7 @@ bool tiles_ok(const decode_attn_shape_t* s) {
   if (t->attn_workgroups < 0 || t->attn_workgroups > kMaxAttnWorkgroups) return false;
   if (t->attn_depth < 0 || t->attn_depth > 3) return false;
   if (t->proj_ksplit < 0 || t->step_mode < 0 || t->step_mode > 2) return false;
+  if (t->step_wait_polls < 0 || t->step_wait_polls > (1 << 24)) return false;
   if (const int tn = t->proj_tile_n) {
     if (tn != 64 && tn != 128 && tn != 256 && tn != 512) return false;
     // 128 is the MFMA GEMM's tile; the other widths ask for the GEMV (batch < 16)
@@ -210,14 +211,6 @@ constexpr int kStepResident = 512;        // workgroups resident at once: two 25
 constexpr int kStepAttnTarget = 128;      // attention workgroups aimed at
 constexpr int kStepMaxAttn = 384;         // at most, leaving room for the projection
 constexpr int kPieceGrain = 128;          // keys of a piece: a multiple of 4 waves x 32 keys
-// The projection may request its weight kStepWeightDelay ticks (100 MHz)
-// after it starts, to let the attention's first loads go ahead. Measured on
-// the 32/8-head, 2048-key, 4096-hidden step: 1.5 us of delay gains ~1.3 us
-// per step when the inputs are cache-resident but loses ~0.3 us when they
-// come from HBM, so it is off.
-constexpr uint32_t kStepWeightDelay = 0;
-constexpr uint32_t kStepStageGap = 0;     // ticks between the 8 stages of those requests
-
 struct StepPlan {
   bool ok;
   int gpad, mpad;
@@ -441,7 +434,7 @@ int run_step(const void* q, const void* k, const void* v, const int32_t* sl, con
   p.seq_cnt = cnt;
   p.proj_cnt = cnt + s->batch * s->num_kv_heads * da::kStepReplicas * da::kCounterStride;
   p.pass_top = cnt + da::kStepCounterBase;
-  p.error = cnt + da::kStepCounterBase + 1;
+  p.error = cnt + da::kStepErrorWord;
   p.pass_sub = cnt + da::kStepCounterBase + 32;
   p.B = s->batch;
   p.Hq = s->num_q_heads;
@@ -454,8 +447,7 @@ int run_step(const void* q, const void* k, const void* v, const int32_t* sl, con
   p.attn_wgs = sp.attn_wgs;
   p.tiles = sp.tiles;
   p.chunks = sp.chunks;
-  p.weight_delay = kStepWeightDelay;
-  p.stage_gap = kStepStageGap;
+  p.wait_polls = s->tiles && s->tiles->step_wait_polls ? (uint32_t)s->tiles->step_wait_polls : da::kStepWaitPolls;
   const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
   p.scale_log2 = scale * 1.4426950408889634f;
   return da::launch_decode_step(p, sp.gpad, sp.mpad, sp.tile_n, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
@@ -632,6 +624,18 @@ int prefill_attn_fwd(const void* q, const void* k_cache, const void* v_cache, co
   return da::launch_prefill(p, (hipStream_t)stream) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
+int decode_attn_step_status(const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return DA_ERR_NULL;
+  if (workspace_bytes < da::kCounterBlockBytes) return DA_ERR_WORKSPACE;
+  if (misaligned(workspace, kAlign)) return DA_ERR_ALIGN;
+  uint32_t word = 0;
+  hipStream_t st = (hipStream_t)stream;
+  const uint32_t* src = (const uint32_t*)workspace + da::kStepErrorWord;
+  if (hipMemcpyAsync(&word, src, sizeof word, hipMemcpyDeviceToHost, st) != hipSuccess) return DA_ERR_LAUNCH;
+  if (hipStreamSynchronize(st) != hipSuccess) return DA_ERR_LAUNCH;
+  return word == 0 ? DA_OK : DA_ERR_TIMEOUT;
+}
+
 const char* decode_attn_status_str(int status) {
   switch (status) {
     case DA_OK: return "ok";
@@ -640,6 +644,8 @@ const char* decode_attn_status_str(int status) {
     case DA_ERR_ALIGN: return "misaligned pointer (16-byte tensors, 256-byte workspace)";
     case DA_ERR_WORKSPACE: return "workspace missing or too small";
     case DA_ERR_LAUNCH: return "kernel launch failed";
+    case DA_ERR_TIMEOUT: return "a single-launch step stopped waiting for its attention (outputs invalid; "
+                                "zero-fill the workspace counters again)";
     default: return "unknown status";
   }
 }

@@ -54,12 +54,6 @@ __device__ __forceinline__ uint4 rsrc_ld16_coherent(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint2 rsrc_ld8_coherent(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCachePolicySc1));
 }
-__device__ __forceinline__ float rsrc_ld4f_coherent(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCachePolicySc1));
-}
-__device__ __forceinline__ void rsrc_st4f_coherent(rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, (int)off, 0, kCachePolicySc1);
-}
 __device__ __forceinline__ void rsrc_st16_coherent(rsrc_t r, uint32_t off, uint4 v) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kCachePolicySc1);

@@ -22,9 +22,10 @@
 // memory, and no workgroup waits for heads it does not use.
 // Workgroups are dispatched in index order, so every attention workgroup is
 // running before a projection workgroup waits; the waits are bounded (a
-// workgroup that gives up sets `error`). The last projection workgroup to pass
-// its wait returns seq_cnt to zero, counted in two levels (32 counters, then
-// one) so that no single address takes more than a few dozen atomics.
+// workgroup that gives up sets `error` and writes NaN). The last projection
+// workgroup to pass its wait, counted in two levels (32 counters, then one) so
+// that no single address takes more than a few dozen atomics, checks that
+// every piece has been counted and returns seq_cnt to zero.
 #include "attn_core.hpp"
 #include "gemv_core.hpp"
 
@@ -35,10 +36,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kPassGroups = 32;
-constexpr uint32_t kWaitPolls = 1u << 20;  // a fraction of a second of polling before giving up
 constexpr int kMergeLoads = 8;             // pieces whose loads are in flight together in the merge
 constexpr int kRowsPerLane = 32;           // weight rows a projection lane holds (16 bytes each)
-constexpr int kWeightStages = 8;           // the weight tile is requested in this many steps
 constexpr uint32_t kNoLoad = 0x80000000u;  // buffer offset past every range: the load returns 0, no request
 
 // ---- attention: piece `a` = (sequence a / pieces, piece a % pieces) ----
@@ -138,7 +137,7 @@ __device__ __forceinline__ void projection(const StepParams& p, int r, char* sme
   constexpr int UR = kRowsPerLane;
   constexpr int KC = UR * RPP;            // rows of the K-chunk
   constexpr int NH = KC / kHeadDim;       // query heads of the chunk
-  static_assert(NH >= 1 && UR % kWeightStages == 0, "chunk of whole query heads, staged loads");
+  static_assert(NH >= 1, "chunk of whole query heads");
   constexpr int kFinOff = (KC * MB + 6 * kThreads) * 4;
   static_assert(kFinOff + gemv_finish_lds<MB, TC>() <= kAttnLds, "projection scratch fits the kernel's LDS");
   float* const s_x = reinterpret_cast<float*>(smem);  // [row of the chunk][MB] attention output, fp32 of bf16
@@ -151,38 +150,41 @@ __device__ __forceinline__ void projection(const StepParams& p, int r, char* sme
   const int rr = t / LPR;
   DA_TRACE(8);
 
-  // the whole weight tile of this workgroup, requested in stages after a delay
-  // (the attention's dependent loads go first) and held in registers. Loads
-  // return in order, so the wave that polls below (wave 0) requests all of
-  // its rows in the first stage: its polls then wait only for those.
+  // the whole weight tile of this workgroup, requested at once and held in
+  // registers, so that it streams while the attention runs. Loads return in
+  // order, so the wave that polls below (wave 0) waits only for its own rows.
   uint4 wv[UR];
   const uint16_t* wrow = p.w + (size_t)(chunk * KC + rr) * p.N + n;
-  const uint64_t t0 = wall_clock64();
-  const uint32_t gap = t < kWave ? 0u : p.stage_gap;
 #pragma unroll
-  for (int st = 0; st < kWeightStages; ++st) {
-    const uint64_t due = p.weight_delay + (uint64_t)st * gap;
-    while (due && wall_clock64() - t0 < due) __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-    for (int u = st * (UR / kWeightStages); u < (st + 1) * (UR / kWeightStages); ++u)
-      wv[u] = n < p.N ? ld16(wrow + (size_t)u * RPP * p.N) : make_uint4(0, 0, 0, 0);
-  }
+  for (int u = 0; u < UR; ++u) wv[u] = n < p.N ? ld16(wrow + (size_t)u * RPP * p.N) : make_uint4(0, 0, 0, 0);
 
-  // wait until every piece of the chunk's kv heads (all batch rows) is stored
+  // wait until every piece of the chunk's kv heads (all batch rows) is stored.
+  // The wait is bounded: a workgroup that gives up sets the error word, which
+  // the host reads back (decode_attn_step_status), and its output tile becomes
+  // NaN so that the failure cannot pass for a result.
+  __shared__ uint32_t s_flags;  // bit 0: this workgroup gave up; bit 1: it clears the piece counters
   const int qh0 = chunk * NH;
   const int h0 = qh0 / p.G, nkv = (qh0 + NH - 1) / p.G - h0 + 1;
   if (t == 0) {
     uint32_t polls = 0;
-    for (int m = 0; m < p.B; ++m)
-      for (int hh = 0; hh < nkv; ++hh) {
+    bool ok = true;
+    for (int m = 0; m < p.B && ok; ++m)
+      for (int hh = 0; hh < nkv && ok; ++hh) {
         const uint32_t* c = &p.seq_cnt[((m * p.Hkv + h0 + hh) * kStepReplicas + r % kStepReplicas) * kCounterStride];
-        while (polls < kWaitPolls &&
-               __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.pieces) {
+        while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.pieces) {
+          if (++polls >= p.wait_polls) {
+            ok = false;
+            break;
+          }
           __builtin_amdgcn_s_sleep(8);
-          if (++polls == kWaitPolls) __hip_atomic_store(p.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
+    if (!ok) {
+      __hip_atomic_store(p.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_stores_done();  // the error word is in place before this workgroup counts itself past the wait
+    }
     // count this workgroup past its wait; the last one clears the piece counters
+    uint32_t flags = ok ? 0u : 1u;
     const int P = (int)gridDim.x - p.attn_wgs;
     const int g = r % kPassGroups;
     const uint32_t in_group = (uint32_t)(P / kPassGroups + (g < P % kPassGroups ? 1 : 0));
@@ -191,12 +193,39 @@ __device__ __forceinline__ void projection(const StepParams& p, int r, char* sme
       const uint32_t ngroups = (uint32_t)min(P, kPassGroups);
       if (__hip_atomic_fetch_add(p.pass_top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1) {
         __hip_atomic_store(p.pass_top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int i = 0; i < p.B * p.Hkv * kStepReplicas; ++i)
-          __hip_atomic_store(&p.seq_cnt[i * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        flags |= 2u;
       }
     }
+    s_flags = flags;
   }
   __syncthreads();
+  if (s_flags & 2u) {
+    // Every workgroup is past its wait. Before the piece counters return to
+    // zero, every copy of every sequence's counter must be complete: a copy
+    // that no workgroup polled may still have an increment in flight. If a
+    // copy stays short (some workgroup gave up), the counters stay as they
+    // are and the error word is set; the caller zero-fills them again.
+    const int ncnt = p.B * p.Hkv * kStepReplicas;
+    bool done = __hip_atomic_load(p.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
+    for (int i = t; i < ncnt && done; i += kThreads) {
+      const uint32_t* c = &p.seq_cnt[i * kCounterStride];
+      uint32_t polls = 0;
+      while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.pieces) {
+        if (++polls >= p.wait_polls) {
+          done = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+    done = __syncthreads_and(done);
+    if (done) {
+      for (int i = t; i < ncnt; i += kThreads)
+        __hip_atomic_store(&p.seq_cnt[i * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (t == 0) {
+      __hip_atomic_store(p.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   DA_TRACE(9);
 
   // merge the pieces of the chunk's heads: (batch row, head, 4 dims) per lane,
@@ -279,6 +308,12 @@ __device__ __forceinline__ void projection(const StepParams& p, int r, char* sme
     }
   }
   DA_TRACE(11);
+  if (s_flags & 1u) {
+#pragma unroll
+    for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[mm][e] = __builtin_nanf("");
+  }
 
   GemvParams g{};
   g.out = p.out;

@@ -9,9 +9,7 @@ namespace da {
 
 // ---- target facts (checked against hipGetDeviceProperties in the tests) ----
 constexpr int kWave = 64;              // wavefront width
-constexpr int kLdsBytesPerCU = 163840; // 160 KiB of LDS per compute unit
-constexpr int kHeadDim = 128;          // the only head_dim implemented
-constexpr int kMaxGroup = 16;          // one 16-row MFMA operand holds a query group
+constexpr int kHeadDim = 128;          // head_dim of the single-launch step and the context attention
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -54,34 +52,8 @@ __device__ __forceinline__ f32x4_t mfma_f16(const uint4& a, const uint4& b, f32x
                                                 0, 0, 0);
 }
 
-// ---- cross-lane reductions inside a 16-lane DPP row --------------------------
-// dpp_ctrl encodings (GFX9 DPP): quad_perm [1,0,3,2] = 0xb1, quad_perm
-// [2,3,0,1] = 0x4e, row_half_mirror = 0x141, row_mirror = 0x140.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f32<0xb1>(x));
-  x = fmaxf(x, dpp_f32<0x4e>(x));
-  x = fmaxf(x, dpp_f32<0x141>(x));
-  x = fmaxf(x, dpp_f32<0x140>(x));
-  return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f32<0xb1>(x);
-  x += dpp_f32<0x4e>(x);
-  x += dpp_f32<0x141>(x);
-  x += dpp_f32<0x140>(x);
-  return x;
-}
-
 // A value that is the same in every lane, moved to a scalar register.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ __forceinline__ float readlane_f32(float x, int lane) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
-}
 
 // Orders LDS traffic of one wavefront (a compiler barrier; LDS requests of a
 // wave are served in issue order).
@@ -98,12 +70,6 @@ __device__ __forceinline__ void wave_lds_fence() {
 // another therefore goes through device-scope (sc1) stores and loads, which
 // are made coherent at device level, instead of ordinary stores followed by a
 // device-wide fence (that fence writes back and invalidates the whole L2).
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // Wait until every store this thread issued has been acknowledged.
 __device__ __forceinline__ void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -127,8 +93,7 @@ __device__ __forceinline__ bool arrive_last_coherent(uint32_t* counter, uint32_t
   return last;
 }
 
-// 16-byte global load / store.
+// 16-byte global load.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 }  // namespace da

@@ -91,13 +91,12 @@ struct StepParams {
   uint32_t* proj_cnt;       // arrival counters of the K-chunks per column tile (chunks > 1), one per line
   uint32_t* pass_sub;       // [32] projection workgroups past their wait, by index mod 32
   uint32_t* pass_top;       // groups of pass_sub that are complete
-  uint32_t* error;          // set to 1 when a projection workgroup stopped waiting
+  uint32_t* error;          // set to 1 when a projection workgroup stopped waiting (read by the host)
   int B, Hq, Hkv, G, Lmax, N;
   int piece_keys, pieces;   // keys per piece (a multiple of 128), pieces per sequence
   int attn_wgs;             // B * Hkv * pieces
   int tiles, chunks;        // projection: column tiles x K-chunks (query heads of one kv head or whole kv heads)
-  uint32_t weight_delay;    // 100 MHz ticks a projection workgroup waits before its first weight loads
-  uint32_t stage_gap;       // ticks between its 8 stages of weight loads
+  uint32_t wait_polls;      // polls of a counter before a projection workgroup gives up waiting (>= 1)
   float scale_log2;         // softmax scale * log2(e)
 };
 
@@ -110,6 +109,8 @@ constexpr int kStepReplicas = 4;
 
 // Fixed slots of the counter block used by the single-launch step.
 constexpr int kStepCounterBase = kMaxCounters - 64;  // pass_top, error, then pass_sub[32] at +32
+constexpr int kStepErrorWord = kStepCounterBase + 1;  // the error word, read back by decode_attn_step_status
+constexpr uint32_t kStepWaitPolls = 1u << 20;         // default bound of a projection workgroup's wait
 
 // Shapes the single-launch step is built for: query group (padded), batch rows
 // (padded) and tile_n output columns per projection workgroup, whose K-chunk

@@ -1,8 +1,8 @@
 // Context (prefill) attention of a chunk of new tokens on gfx950.
 //
-// The F-16 page ("PyPTO 开箱性能调优实战：Decode Attention 多 Matmul 独立
-// TileShape 配置 F-16") names a context-attention kernel next to the decode one
-// without defining it; the reading taken here: sequence b holds ctx_lens[b]
+// The page "CCCL → Triton 方法论迁移" (section 二, 2.1 prefix_prefill.py)
+// names a context attention next to the decode attention and gives only its
+// tile knobs; the reading taken here: sequence b holds ctx_lens[b]
 // cached keys, the last T of which are the chunk's own tokens, and token t
 // attends causally to keys 0 .. ctx_lens[b] - T + t with the decode step's
 // scaled softmax (T = 1 is the decode attention).

@@ -46,6 +46,8 @@ extern "C" {
 #define DA_ERR_ALIGN (-3)     /* a base address is not 16-byte aligned                */
 #define DA_ERR_WORKSPACE (-4) /* workspace missing or smaller than required          */
 #define DA_ERR_LAUNCH (-5)    /* a kernel launch failed (hipGetLastError after it)   */
+#define DA_ERR_TIMEOUT (-6)   /* decode_attn_step_status: a single-launch step stopped
+                                 waiting for its attention pieces (see there)        */
 
 /* head_dim: 128 (every path) or DA_HEAD_DIM_WIDE (stream-K attention and the
  * separate projection; the single-launch step is built for 128 only). */
@@ -83,6 +85,9 @@ extern "C" {
  *                   every chunk is a whole number of the kernel's row batches)
  *  step_mode        0 built-in, 1 one launch where the single-launch step
  *                   supports the shape, 2 two launches (as DA_FLAG_SEPARATE)
+ *  step_wait_polls  bound of the single-launch step's waits, in polls of a
+ *                   counter, 1..2^24 (built-in 2^20, a fraction of a second);
+ *                   a workgroup that reaches it gives up (decode_attn_step_status)
  */
 typedef struct {
   int32_t attn_workgroups;
@@ -90,6 +95,7 @@ typedef struct {
   int32_t proj_tile_n;
   int32_t proj_ksplit;
   int32_t step_mode;
+  int32_t step_wait_polls;
 } decode_attn_tiles_t;
 
 /*
@@ -184,6 +190,27 @@ int decode_attn_fwd(const void* q_dev, const void* k_cache_dev, const void* v_ca
                     const int32_t* seq_lens_dev, const void* o_weight_dev, void* out_dev,
                     const decode_attn_shape_t* shape, void* stream);
 
+/*
+ * Status of the single-launch steps run on a workspace since its counter block
+ * was last zero-filled. In that launch (decode_attn_plan's `fused`), the
+ * projection workgroups wait for the attention pieces of their kv heads, and
+ * each wait is bounded (decode_attn_tiles_t.step_wait_polls). One that gives up
+ * sets an error word in the workspace's counter block, writes NaN to its
+ * output columns and leaves the counters dirty. This call waits for `stream`
+ * (a hipStream_t as void*, NULL = the default stream) to drain, reads that word
+ * and returns:
+ *   DA_OK           no wait gave up;
+ *   DA_ERR_TIMEOUT  some wait gave up: the outputs of those calls are invalid
+ *                   (NaN), and the first 64 KiB of the workspace must be
+ *                   zero-filled again before its next use;
+ *   DA_ERR_NULL / DA_ERR_WORKSPACE (workspace NULL or under 64 KiB) before any
+ *                   HIP call, DA_ERR_ALIGN (not 256-byte aligned), or
+ *                   DA_ERR_LAUNCH if the copy or the synchronisation fails.
+ * It blocks the host, so it cannot be captured into a graph. Two-launch steps
+ * never wait and never set the word.
+ */
+int decode_attn_step_status(const void* workspace, size_t workspace_bytes, void* stream);
+
 /* The first two matmuls and the softmax only: attn_out_dev receives the
  * bf16 [B, Hq*D] head-major attention output (attn_output_flat). */
 int decode_attn_only(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
@@ -213,8 +240,9 @@ int oproj_fwd(const void* x_dev, const void* w_dev, void* out_dev, int32_t M, in
 int gemm_f16(const void* a_dev, const void* b_dev, void* c_dev, int32_t M, int32_t N, int32_t K, void* stream);
 
 /*
- * Context (prefill) attention of a chunk of new tokens. The F-16 page names a
- * context-attention kernel beside the decode one without defining it; read
+ * Context (prefill) attention of a chunk of new tokens. The page "CCCL →
+ * Triton 方法论迁移" (section 二, 2.1 prefix_prefill.py) names this context
+ * attention beside the decode attention and gives only its tile knobs; read
  * plainly: sequence b holds ctx_lens[b] cached keys, the last num_tokens of
  * which are the chunk's own tokens (already written to the caches), and token t
  * attends causally to keys 0 .. ctx_lens[b] - num_tokens + t with the decode

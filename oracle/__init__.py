@@ -19,7 +19,8 @@ What each function computes, and the pages it follows:
 * ``decode_step`` -- the three in sequence, the projection reading the bf16
   attention output.
 * ``prefill_attention`` -- context attention of a chunk of new tokens (the
-  same page names a context-attention kernel without defining it; the
+  page "CCCL → Triton 方法论迁移", section 二, 2.1 prefix_prefill.py, names
+  this context attention beside the decode attention without defining it; the
   plainest reading is taken: each token attends causally to the cached keys
   up to its own position, with the decode step's softmax). T = 1 is exactly
   ``attention``.

@@ -295,8 +295,9 @@ int oracle_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
 /* context (prefill) attention: a chunk of T new tokens per sequence       */
 /* ---------------------------------------------------------------------- */
 /*
- * The pages name a context-attention kernel ("prefix_prefill", Context
- * Attention) next to the decode one but do not spell out what it computes;
+ * The page "CCCL → Triton 方法论迁移" (section 二, 2.1 prefix_prefill.py,
+ * Context Attention) names this kernel next to the decode attention but does
+ * not spell out what it computes;
  * the plainest reading is taken: sequence b holds ctx_lens[b] cached keys,
  * the last T of which belong to the chunk's tokens, and token t (absolute
  * position ctx_lens[b] - T + t) attends causally to keys 0 .. its own

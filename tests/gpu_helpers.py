@@ -10,6 +10,33 @@ REL_FLOOR = 1e-2
 SCORE_TOL = 1e-4         # fp32 scores: |gpu - ref| <= SCORE_TOL * max(|ref|, 1)
 
 
+COUNTER_BLOCK = 65536    # the first bytes of every workspace: arrival counters, zero between calls
+
+
+class PoisonedWorkspace:
+    """A workspace whose scratch data (every byte past the counter block) is
+    refilled with 0xFF -- NaN as fp32 and as bf16 -- on the call's stream before
+    every call, so that a read of a partial result that was never written shows
+    up as NaN in the output instead of passing as a stale or zero value."""
+
+    def __init__(self, device=None):
+        import decode_attention_output_amd as da
+
+        self._ws = da.Workspace(device)
+
+    @property
+    def buf(self):
+        return self._ws.buf
+
+    def get(self, nbytes: int, stream=None):
+        buf = self._ws.get(nbytes, stream)
+        if buf is not None and buf.numel() > COUNTER_BLOCK:
+            s = stream if stream is not None else torch.cuda.current_stream()
+            with torch.cuda.stream(s):
+                buf[COUNTER_BLOCK:].fill_(0xFF)
+        return buf
+
+
 def dev_bf16(words: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(words).view(np.int16)).view(torch.bfloat16).to(device)
 

@@ -40,7 +40,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (da.DA_OK, da.DA_ERR_NULL, da.DA_ERR_SHAPE, da.DA_ERR_ALIGN, da.DA_ERR_WORKSPACE, da.DA_ERR_LAUNCH):
+    for code in (da.DA_OK, da.DA_ERR_NULL, da.DA_ERR_SHAPE, da.DA_ERR_ALIGN, da.DA_ERR_WORKSPACE, da.DA_ERR_LAUNCH,
+                 da.DA_ERR_TIMEOUT):
         assert da.status_str(code) and da.status_str(code) != "unknown status"
     assert da.status_str(-99) == "unknown status"
 
@@ -107,6 +108,20 @@ def test_oproj_and_gemm_argument_checks(lib):
     assert lib.gemm_f16(FAKE, None, FAKE, 256, 512, 1024, None) == da.DA_ERR_NULL
     assert lib.gemm_f16(FAKE, FAKE, FAKE, 250, 512, 1024, None) == da.DA_ERR_SHAPE
     assert lib.gemm_f16(FAKE, FAKE, FAKE, 256, 512, 1000, None) == da.DA_ERR_SHAPE
+
+
+def test_step_status_argument_checks(lib):
+    # all rejected before any HIP call (no device here)
+    assert lib.decode_attn_step_status(None, 1 << 20, None) == da.DA_ERR_NULL
+    assert lib.decode_attn_step_status(FAKE, 65535, None) == da.DA_ERR_WORKSPACE
+    assert lib.decode_attn_step_status(FAKE + 16, 1 << 20, None) == da.DA_ERR_ALIGN
+    # a workspace the binding never allocated has seen no single-launch step
+    assert da.decode_attn_step_status(da.Workspace()) == da.DA_OK
+
+
+def test_step_wait_polls_in_range_is_accepted(lib):
+    for polls in (1, 1000, 1 << 24):
+        assert da.decode_attn_workspace_size(_shape(tiles=dict(step_wait_polls=polls))) > 0
 
 
 def _golden_shapes():
@@ -187,7 +202,8 @@ def test_plan_fuses_small_steps_only(lib, cfg):
 
 @pytest.mark.parametrize("tiles", [dict(attn_workgroups=-1), dict(attn_workgroups=1025), dict(attn_depth=4),
                                    dict(attn_depth=-2), dict(proj_tile_n=96), dict(proj_tile_n=1024),
-                                   dict(proj_ksplit=-1), dict(step_mode=3)])
+                                   dict(proj_ksplit=-1), dict(step_mode=3), dict(step_wait_polls=-1),
+                                   dict(step_wait_polls=(1 << 24) + 1)])
 def test_tile_override_out_of_range_is_a_shape_error(lib, tiles):
     shape = _shape(tiles=tiles)
     assert da.decode_attn_workspace_size(shape) == 0
