@@ -9,7 +9,7 @@ raises.
 The names mirror the C entry points: ``decode_attn_fwd``, ``decode_attn_only``,
 ``oproj_fwd``, ``gemm_f16``, ``decode_attn_workspace_size``,
 ``oproj_workspace_size``, ``decode_attn_plan``, ``decode_attn_status_str``,
-``prefill_attn_fwd``, ``decode_attn_step_status``.
+``prefill_attn_fwd``, ``decode_attn_step_status``, ``decode_attn_fwd_noalloc``.
 
 Before any call reaches the library, the torch wrappers check that the
 tensors agree with each other (batch, heads, head_dim, cache length,
@@ -49,6 +49,7 @@ EXPORTED = (
     "decode_attn_status_str",
     "prefill_attn_fwd",
     "decode_attn_step_status",
+    "decode_attn_fwd_noalloc",
 )
 
 
@@ -148,6 +149,8 @@ def load_library(path: str = LIB_PATH):
     lib.gemm_f16.argtypes = [vp, vp, vp, i32, i32, i32, vp]
     lib.prefill_attn_fwd.restype = ctypes.c_int
     lib.prefill_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(PrefillAttnShape), vp]
+    lib.decode_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.decode_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, shp, vp]
     lib.decode_attn_step_status.restype = ctypes.c_int
     lib.decode_attn_step_status.argtypes = [vp, sz, vp]
     lib.decode_attn_status_str.restype = ctypes.c_char_p
@@ -338,7 +341,10 @@ class Workspace:
 
 def decode_attn_step_status(workspace, stream=None) -> int:
     """DA_OK, or DA_ERR_TIMEOUT if a single-launch step on this workspace gave up
-    waiting since its counters were last zero-filled (waits for the stream)."""
+    waiting since its counters were last zero-filled (waits for the stream).
+    ``workspace=None`` asks about the no-allocation scratch of the current device."""
+    if workspace is None:
+        return int(load_library().decode_attn_step_status(None, 0, _stream_handle(stream)))
     buf = getattr(workspace, "buf", workspace)
     if buf is None:
         return DA_OK  # never used: no single-launch step ran on it
@@ -372,6 +378,23 @@ def decode_attn_fwd(q, k_cache, v_cache, seq_lens, o_weight, out=None, workspace
                                         _stream_handle(stream))
     if rc != DA_OK:
         raise DecodeAttnError(rc, "decode_attn_fwd")
+    return out
+
+
+def decode_attn_fwd_noalloc(q, k_cache, v_cache, seq_lens, o_weight, out, softmax_scale: float = 0.0, stream=None,
+                            separate=False, tiles=None):
+    """decode_attn_fwd on the library's own scratch array: no workspace, and no
+    allocation by the library; ``out`` [B, hidden] bf16 is the caller's."""
+    B, Hq, Hkv, D, Lmax, hidden = check_decode_tensors(q, k_cache, v_cache, seq_lens, o_weight, out)
+    if out is None:
+        raise ValueError("decode_attn_fwd_noalloc writes into the caller's out tensor")
+    shape = make_shape(B, Hq, Hkv, Lmax, hidden, D, softmax_scale, flags=DA_FLAG_SEPARATE if separate else 0,
+                       tiles=tiles)
+    rc = load_library().decode_attn_fwd_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                                seq_lens.data_ptr(), o_weight.data_ptr(), out.data_ptr(),
+                                                ctypes.byref(shape), _stream_handle(stream))
+    if rc != DA_OK:
+        raise DecodeAttnError(rc, "decode_attn_fwd_noalloc")
     return out
 
 

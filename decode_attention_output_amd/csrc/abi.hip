@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/decode_attn.h"
 #include "gfx950.hpp"
@@ -453,6 +454,103 @@ int run_step(const void* q, const void* k, const void* v, const int32_t* sl, con
   return da::launch_decode_step(p, sp.gpad, sp.mpad, sp.tile_n, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
+// ---- the no-allocation entry point's scratch: one array per device ----
+//
+// decode_attn_fwd_noalloc takes its workspace from this array instead of the
+// caller. Host code never uses the array's name as an address (on the host it
+// is only a stand-in for the symbol): every kernel argument, fill and copy
+// uses the device address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+constexpr size_t kScratchBytes = (size_t)DA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+__global__ void zero_counter_block(uint32_t* words) { words[blockIdx.x * blockDim.x + threadIdx.x] = 0u; }
+
+struct ScratchSlot {
+  void* ptr;           // device address of `scratch` on this device
+  bool needs_clear;    // its counter block is to be zero-filled before the next call
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+// The scratch address of the current device (*dev); the first call on a
+// device looks it up. *clear tells whether its counter block must be
+// zero-filled first (mark_cleared once that is enqueued).
+int scratch_of_current_device(void** ptr, bool* clear, int* dev) {
+  *dev = -1;
+  if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= kMaxDevices) return DA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& slot = g_scratch[*dev];
+  if (!slot.ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DA_ERR_LAUNCH;
+    slot.ptr = p;
+    slot.needs_clear = true;
+  }
+  *ptr = slot.ptr;
+  *clear = slot.needs_clear;
+  return DA_OK;
+}
+
+void mark_cleared(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  g_scratch[dev].needs_clear = false;
+}
+
+// Zero-fill a workspace's counter block on `st` with a kernel (no memset node
+// ends up in a graph that captures the call).
+int clear_counter_block(void* ws, hipStream_t st) {
+  constexpr int kWords = (int)(da::kCounterBlockBytes / sizeof(uint32_t));
+  zero_counter_block<<<dim3(kWords / 256), dim3(256), 0, st>>>((uint32_t*)ws);
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+// decode_attn_fwd, with the caller's workspace or (noalloc) the scratch array.
+int fwd_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, const void* o_weight,
+             void* out, const decode_attn_shape_t* shape_in, void* stream, bool noalloc) {
+  if (!shape_in) return DA_ERR_NULL;
+  decode_attn_shape_t eff = effective_shape(shape_in);
+  const decode_attn_shape_t* shape = &eff;
+  int rc = check_attn_ptrs(q, k_cache, v_cache, seq_lens, out);
+  if (rc) return rc;
+  if (!o_weight) return DA_ERR_NULL;
+  if (misaligned(o_weight, 16)) return DA_ERR_ALIGN;
+  if (!shape_ok(shape, true)) return DA_ERR_SHAPE;
+  const Layout L = layout_for(shape, true);
+  if (!L.fits) return DA_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (noalloc) {
+    if (L.total > kScratchBytes) return DA_ERR_WORKSPACE;
+    if ((rc = check_debug(shape))) return rc;
+    void* ptr = nullptr;
+    bool clear = false;
+    int dev = -1;
+    if ((rc = scratch_of_current_device(&ptr, &clear, &dev))) return rc;
+    if (clear) {
+      if ((rc = clear_counter_block(ptr, st))) return rc;
+      mark_cleared(dev);
+    }
+    eff.workspace = ptr;
+    eff.workspace_bytes = kScratchBytes;
+  } else {
+    if ((rc = check_workspace(shape, L.total))) return rc;
+    if ((rc = check_debug(shape))) return rc;
+  }
+  char* ws = (char*)shape->workspace;
+  void* flat = ws + L.off_flat;
+  const da::AttnParams p = attn_params(q, k_cache, v_cache, seq_lens, flat, shape, L);
+  if (L.fused) return run_step(q, k_cache, v_cache, seq_lens, o_weight, out, shape, L, st);
+  if ((rc = run_attention(p, L, st))) return rc;
+  return run_proj(L.proj, flat, o_weight, out, shape->batch, shape->num_q_heads * shape->head_dim, shape->hidden,
+                  ws + L.off_proj_part, (char*)((uint32_t*)ws + L.proj_counter0), st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -512,26 +610,12 @@ int decode_attn_plan(const decode_attn_shape_t* shape_in, decode_attn_plan_t* pl
 
 int decode_attn_fwd(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                     const void* o_weight, void* out, const decode_attn_shape_t* shape_in, void* stream) {
-  if (!shape_in) return DA_ERR_NULL;
-  const decode_attn_shape_t eff = effective_shape(shape_in);
-  const decode_attn_shape_t* shape = &eff;
-  int rc = check_attn_ptrs(q, k_cache, v_cache, seq_lens, out);
-  if (rc) return rc;
-  if (!o_weight) return DA_ERR_NULL;
-  if (misaligned(o_weight, 16)) return DA_ERR_ALIGN;
-  if (!shape_ok(shape, true)) return DA_ERR_SHAPE;
-  const Layout L = layout_for(shape, true);
-  if (!L.fits) return DA_ERR_SHAPE;
-  if ((rc = check_workspace(shape, L.total))) return rc;
-  if ((rc = check_debug(shape))) return rc;
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)shape->workspace;
-  void* flat = ws + L.off_flat;
-  const da::AttnParams p = attn_params(q, k_cache, v_cache, seq_lens, flat, shape, L);
-  if (L.fused) return run_step(q, k_cache, v_cache, seq_lens, o_weight, out, shape, L, st);
-  if ((rc = run_attention(p, L, st))) return rc;
-  return run_proj(L.proj, flat, o_weight, out, shape->batch, shape->num_q_heads * shape->head_dim, shape->hidden,
-                  ws + L.off_proj_part, (char*)((uint32_t*)ws + L.proj_counter0), st);
+  return fwd_impl(q, k_cache, v_cache, seq_lens, o_weight, out, shape_in, stream, false);
+}
+
+int decode_attn_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                            const void* o_weight, void* out, const decode_attn_shape_t* shape, void* stream) {
+  return fwd_impl(q, k_cache, v_cache, seq_lens, o_weight, out, shape, stream, true);
 }
 
 int decode_attn_only(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
@@ -625,15 +709,32 @@ int prefill_attn_fwd(const void* q, const void* k_cache, const void* v_cache, co
 }
 
 int decode_attn_step_status(const void* workspace, size_t workspace_bytes, void* stream) {
-  if (!workspace) return DA_ERR_NULL;
-  if (workspace_bytes < da::kCounterBlockBytes) return DA_ERR_WORKSPACE;
-  if (misaligned(workspace, kAlign)) return DA_ERR_ALIGN;
-  uint32_t word = 0;
+  const bool own = workspace == nullptr;  // the no-allocation scratch of the current device
+  if (!own) {
+    if (workspace_bytes < da::kCounterBlockBytes) return DA_ERR_WORKSPACE;
+    if (misaligned(workspace, kAlign)) return DA_ERR_ALIGN;
+  }
   hipStream_t st = (hipStream_t)stream;
+  if (own) {
+    void* ptr = nullptr;
+    bool clear = false;
+    int dev = -1;
+    const int rc = scratch_of_current_device(&ptr, &clear, &dev);
+    if (rc) return rc;
+    if (clear) return DA_OK;  // no call has run on it yet
+    workspace = ptr;
+  }
+  uint32_t word = 0;
   const uint32_t* src = (const uint32_t*)workspace + da::kStepErrorWord;
   if (hipMemcpyAsync(&word, src, sizeof word, hipMemcpyDeviceToHost, st) != hipSuccess) return DA_ERR_LAUNCH;
   if (hipStreamSynchronize(st) != hipSuccess) return DA_ERR_LAUNCH;
-  return word == 0 ? DA_OK : DA_ERR_TIMEOUT;
+  if (word == 0) return DA_OK;
+  if (own) {
+    // the caller cannot reach the scratch: its counter block is zero-filled here
+    if (clear_counter_block(const_cast<void*>(workspace), st) != DA_OK) return DA_ERR_LAUNCH;
+    if (hipStreamSynchronize(st) != hipSuccess) return DA_ERR_LAUNCH;
+  }
+  return DA_ERR_TIMEOUT;
 }
 
 const char* decode_attn_status_str(int status) {

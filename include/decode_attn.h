@@ -203,13 +203,35 @@ int decode_attn_fwd(const void* q_dev, const void* k_cache_dev, const void* v_ca
  *   DA_ERR_TIMEOUT  some wait gave up: the outputs of those calls are invalid
  *                   (NaN), and the first 64 KiB of the workspace must be
  *                   zero-filled again before its next use;
- *   DA_ERR_NULL / DA_ERR_WORKSPACE (workspace NULL or under 64 KiB) before any
- *                   HIP call, DA_ERR_ALIGN (not 256-byte aligned), or
- *                   DA_ERR_LAUNCH if the copy or the synchronisation fails.
+ *   DA_ERR_WORKSPACE (under 64 KiB) or DA_ERR_ALIGN (not 256-byte aligned)
+ *                   before any HIP call, or DA_ERR_LAUNCH if the copy or the
+ *                   synchronisation fails.
+ * A NULL workspace names the scratch array of decode_attn_fwd_noalloc on the
+ * current device; after a timeout there, this call zero-fills its counters.
  * It blocks the host, so it cannot be captured into a graph. Two-launch steps
  * never wait and never set the word.
  */
 int decode_attn_step_status(const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * decode_attn_fwd for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same step, whose workspace is the library's own scratch array of
+ * DA_NOALLOC_SCRATCH_BYTES per device instead of shape->workspace (the
+ * workspace fields are ignored). It calls no allocating routine; the first
+ * call on a device looks up that device's array and enqueues a zero fill of
+ * its counters on `stream`. Arguments, layouts and checks are those of
+ * decode_attn_fwd, plus DA_ERR_WORKSPACE (before any HIP call) when the shape
+ * needs more scratch than the array holds. Every call on one device shares
+ * that array and leaves it ready for the next one, so calls that overlap on
+ * one device (different streams, no ordering between them) race and give
+ * wrong results. decode_attn_step_status(NULL, 0, stream) reports this
+ * path's single-launch timeouts and then zero-fills the array's counters.
+ */
+#define DA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int decode_attn_fwd_noalloc(const void* q_dev, const void* k_cache_dev, const void* v_cache_dev,
+                            const int32_t* seq_lens_dev, const void* o_weight_dev, void* out_dev,
+                            const decode_attn_shape_t* shape, void* stream);
 
 /* The first two matmuls and the softmax only: attn_out_dev receives the
  * bf16 [B, Hq*D] head-major attention output (attn_output_flat). */

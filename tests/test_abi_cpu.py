@@ -112,11 +112,26 @@ def test_oproj_and_gemm_argument_checks(lib):
 
 def test_step_status_argument_checks(lib):
     # all rejected before any HIP call (no device here)
-    assert lib.decode_attn_step_status(None, 1 << 20, None) == da.DA_ERR_NULL
     assert lib.decode_attn_step_status(FAKE, 65535, None) == da.DA_ERR_WORKSPACE
     assert lib.decode_attn_step_status(FAKE + 16, 1 << 20, None) == da.DA_ERR_ALIGN
     # a workspace the binding never allocated has seen no single-launch step
     assert da.decode_attn_step_status(da.Workspace()) == da.DA_OK
+
+
+def test_noalloc_entry_checks_arguments_before_any_hip_call(lib):
+    def call(shape, **kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, sl=FAKE, w=FAKE, out=FAKE)
+        a.update(kw)
+        return lib.decode_attn_fwd_noalloc(a["q"], a["k"], a["v"], a["sl"], a["w"], a["out"],
+                                           ctypes.byref(shape) if shape is not None else None, None)
+    assert call(None) == da.DA_ERR_NULL
+    assert call(_shape(), w=None) == da.DA_ERR_NULL
+    assert call(_shape(), out=FAKE + 4) == da.DA_ERR_ALIGN
+    assert call(_shape(num_q_heads=30)) == da.DA_ERR_SHAPE
+    # a step whose workspace exceeds the scratch array: 1024 sequences' attention partials
+    big = _shape(batch=1024, max_seq_len=32768, hidden=8192)
+    assert da.decode_attn_workspace_size(big) > 16 << 20
+    assert call(big) == da.DA_ERR_WORKSPACE
 
 
 def test_step_wait_polls_in_range_is_accepted(lib):
