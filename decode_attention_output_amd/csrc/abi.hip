@@ -29,6 +29,11 @@ using da::kHeadDim;
 constexpr int kAttnWorkgroups = 192;
 constexpr int kMaxAttnWorkgroups = 1024;    // largest stream-K grid a tile override may ask for
 constexpr int kAttnBlockKeys = 32;          // keys per wave step
+// Virtual 32-key blocks a stream-K workgroup is charged for starting a
+// sequence (finishing a piece and restarting take about as long as streaming
+// this many blocks; measured per workgroup on the ragged 16-sequence batch).
+constexpr int kAttnSeqCost = 6;
+constexpr int kMaxAttnSeqCost = 256;
 constexpr int kTargetProjWorkgroups = 512;   // GEMV: two per compute unit
 constexpr int kTargetGemmWorkgroups = 256;   // MFMA GEMM: one per compute unit (measured best of 64..1024)
 constexpr int kGemvUnroll = 8;               // weight rows per lane in flight
@@ -80,6 +85,7 @@ bool tiles_ok(const decode_attn_shape_t* s) {
   if (t->attn_depth < 0 || t->attn_depth > 3) return false;
   if (t->proj_ksplit < 0 || t->step_mode < 0 || t->step_mode > 2) return false;
   if (t->step_wait_polls < 0 || t->step_wait_polls > (1 << 24)) return false;
+  if (t->attn_seq_cost < 0 || t->attn_seq_cost > kMaxAttnSeqCost) return false;
   if (const int tn = t->proj_tile_n) {
     if (tn != 64 && tn != 128 && tn != 256 && tn != 512) return false;
     // 128 is the MFMA GEMM's tile; the other widths ask for the GEMV (batch < 16)
@@ -174,6 +180,7 @@ bool proj_fits(const ProjPlan& pp, int N) {
 // ---- attention: stream-K over the keys of all sequences ----
 struct AttnPlan {
   int gpad;
+  int seq_cost;    // virtual blocks charged per sequence start
   int depth;       // 32-key steps in flight per wave while one is computed
   int workgroups;  // stream-K workgroups
   int keys_per_wg; // upper bound of the keys one workgroup streams
@@ -191,9 +198,11 @@ AttnPlan plan_attn(const decode_attn_shape_t* s) {
   // latency bound and gain nothing from more, smaller pieces
   ap.workgroups = (int)std::max<long>(1, std::min<long>(kAttnWorkgroups, blocks_max / 4));
   ap.depth = 1;
+  ap.seq_cost = kAttnSeqCost;
   if (const decode_attn_tiles_t* t = s->tiles) {
     if (t->attn_workgroups) ap.workgroups = (int)std::max<long>(1, std::min<long>(t->attn_workgroups, blocks_max));
     if (t->attn_depth) ap.depth = t->attn_depth;
+    if (t->attn_seq_cost) ap.seq_cost = t->attn_seq_cost;
   }
   ap.keys_per_wg = ceil_div(blocks_max, ap.workgroups) * kAttnBlockKeys;
   ap.slots = (size_t)ap.workgroups + (size_t)pairs;
@@ -273,9 +282,10 @@ struct Layout {
   ProjPlan proj;
   StepPlan step;
   size_t off_part_o, off_part_ml, off_flat, off_proj_part, total;
-  int attn_counter0, proj_counter0;
+  int attn_counter0, proj_counter0, ready_counter0;
   bool fits;
   bool fused;  // decode_attn_fwd runs the single-launch step
+  bool large;  // decode_attn_fwd runs the single-launch large step (stream-K attention + MFMA GEMM items)
 };
 
 // Workspace: [arrival counters][attention partials][attention output][projection partials]
@@ -304,12 +314,18 @@ Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
     L.proj_counter0 = counters;
     counters += L.proj.tiles;
     L.step = plan_step(s);
+    const bool one_launch = !(s->flags & DA_FLAG_SEPARATE) && !(t && t->step_mode == 2);
     if (L.step.ok) {
       const size_t step_total =
           da::kCounterBlockBytes + L.step.part_o_bytes + L.step.part_ml_bytes + L.step.proj_part_bytes;
       off = std::max(off, step_total);
-      L.fused = !(s->flags & DA_FLAG_SEPARATE) && !(t && t->step_mode == 2);
+      L.fused = one_launch;
     }
+    // the large single-launch step: the two-launch layout plus per-kv-head ready counters
+    L.ready_counter0 = (int)align_up((size_t)counters, da::kCounterStride);
+    const int ready_end = L.ready_counter0 + s->num_kv_heads * da::kStepReplicas * da::kCounterStride;
+    L.large = one_launch && !L.fused && L.proj.path == 1 && L.proj.mtiles <= 2 && s->head_dim == kHeadDim &&
+              !(s->flags & DA_FLAG_DEBUG_SCORES) && ready_end <= da::kStepCounterBase;
   }
   L.total = off;
   L.fits = counters <= da::kStepCounterBase && L.attn.part_o_bytes < (1ull << 32) &&
@@ -363,6 +379,8 @@ da::AttnParams attn_params(const void* q, const void* k, const void* v, const in
   p.head_dim = s->head_dim;
   p.num_workgroups = L.attn.workgroups;
   p.step_variant = L.attn.depth;
+  p.seq_cost = L.attn.seq_cost;
+  p.head_ready = nullptr;
   const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)s->head_dim);
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
@@ -452,6 +470,45 @@ int run_step(const void* q, const void* k, const void* v, const int32_t* sl, con
   const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
   p.scale_log2 = scale * 1.4426950408889634f;
   return da::launch_decode_step(p, sp.gpad, sp.mpad, sp.tile_n, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+// The single-launch large step: stream-K attention workgroups and the MFMA
+// GEMM items of the projection in one grid.
+int run_step_large(const da::AttnParams& attn, const void* w, void* out, const decode_attn_shape_t* s,
+                   const Layout& L, hipStream_t st) {
+  const ProjPlan& pp = L.proj;
+  char* ws = (char*)s->workspace;
+  uint32_t* cnt = (uint32_t*)ws;
+  da::StepLargeParams p{};
+  p.attn = attn;
+  p.attn.head_ready = cnt + L.ready_counter0;
+  da::GemmParams& g = p.gemm;
+  g.a = (const uint16_t*)(ws + L.off_flat);
+  g.b = (const uint16_t*)w;
+  g.c = (uint16_t*)out;
+  g.part = (float*)(ws + L.off_proj_part);
+  g.counters = cnt + L.proj_counter0;
+  g.M = s->batch;
+  g.K = s->num_q_heads * s->head_dim;
+  g.N = s->hidden;
+  g.kchunk = pp.kchunk;
+  g.ksplit = pp.ksplit;
+  g.mtiles = pp.mtiles;
+  g.part_bytes = (uint32_t)std::min<size_t>(pp.part_bytes, 0xffffffffu);
+  p.ntiles = ceil_div(s->hidden, da::kGemmTileN);
+  p.mgroups = ceil_div(s->batch, pp.mpad);
+  da::ReadySync& r = p.wait.sync;
+  r.ready = cnt + L.ready_counter0;
+  r.pass_top = cnt + da::kStepCounterBase;
+  r.error = cnt + da::kStepErrorWord;
+  r.pass_sub = cnt + da::kStepCounterBase + 32;
+  r.heads = s->num_kv_heads;
+  r.target = (uint32_t)s->batch;
+  r.wait_polls = s->tiles && s->tiles->step_wait_polls ? (uint32_t)s->tiles->step_wait_polls : da::kStepWaitPolls;
+  r.waiters = p.ntiles * p.mgroups * pp.ksplit;
+  p.wait.head_dim = s->head_dim;
+  p.wait.group = s->num_q_heads / s->num_kv_heads;
+  return da::launch_decode_step_large(p, L.attn.gpad, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
 // ---- the no-allocation entry point's scratch: one array per device ----
@@ -546,6 +603,7 @@ int fwd_impl(const void* q, const void* k_cache, const void* v_cache, const int3
   void* flat = ws + L.off_flat;
   const da::AttnParams p = attn_params(q, k_cache, v_cache, seq_lens, flat, shape, L);
   if (L.fused) return run_step(q, k_cache, v_cache, seq_lens, o_weight, out, shape, L, st);
+  if (L.large) return run_step_large(p, o_weight, out, shape, L, st);
   if ((rc = run_attention(p, L, st))) return rc;
   return run_proj(L.proj, flat, o_weight, out, shape->batch, shape->num_q_heads * shape->head_dim, shape->hidden,
                   ws + L.off_proj_part, (char*)((uint32_t*)ws + L.proj_counter0), st);
@@ -603,7 +661,7 @@ int decode_attn_plan(const decode_attn_shape_t* shape_in, decode_attn_plan_t* pl
   plan->split_len = L.attn.keys_per_wg;
   plan->num_splits = wgs;
   plan->oproj_path = L.proj.path;
-  plan->fused = 0;
+  plan->fused = L.large ? 2 : 0;
   plan->workspace_bytes = L.total;
   return DA_OK;
 }

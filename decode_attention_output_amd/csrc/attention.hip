@@ -15,6 +15,7 @@ namespace {
 template <int GP, int NW, int D, int HD>
 __global__ __launch_bounds__(NW* kWave, D == 1 ? 2 : 1) void attn_streamk_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char smem[attn_streamk_lds<NW, HD>()];
+  DA_TRACE(14);
   attn_streamk_body<GP, NW, D, HD>(p, blockIdx.x, gridDim.x, smem);
 }
 

@@ -1,16 +1,26 @@
 // The stream-K attention of one workgroup.
 //
 // The keys of all (batch, kv head) sequences are laid end to end as 32-key
-// blocks: sequence (b, h) owns ceil(L_b / 32) consecutive blocks, b-major. The
-// T blocks are cut into W equal contiguous ranges, one per workgroup, so ragged
-// and uniform batches alike give every workgroup the same number of bytes to
-// stream. A workgroup walks its range sequence by sequence; its waves take
+// blocks: sequence (b, h) owns ceil(L_b / 32) consecutive blocks, b-major. In
+// front of every sequence sit `seq_cost` virtual blocks that hold no keys: a
+// workgroup pays for each sequence it starts (finishing a piece, storing its
+// partial, requesting the next piece's first tile) about as much time as it
+// takes to stream a few blocks, so counting that cost in the split keeps the
+// workgroups that cross sequence boundaries from finishing last. The T
+// virtual blocks are cut into W equal contiguous ranges, one per workgroup,
+// so ragged and uniform batches alike give every workgroup the same amount of
+// work. A workgroup walks its range sequence by sequence; its waves take
 // interleaved steps of the piece it is on (attn_core.hpp). A piece that is a
 // whole sequence is normalised and written as bf16 at once; otherwise its
 // un-normalised partial (O, running max, weight sum) goes to a workspace slot
 // through device-coherent stores, and the last workgroup to finish a piece of
 // that sequence (an arrival counter per sequence tells it) merges all of its
 // pieces and writes the bf16 output.
+//
+// In the single-launch large step (kSignal), the bf16 output is written with
+// device-coherent stores and every finished sequence is counted in its kv
+// head's ready counter, which the projection workgroups of the same grid wait
+// for.
 #pragma once
 
 #include "attn_core.hpp"
@@ -37,7 +47,7 @@ constexpr int attn_streamk_lds() {
 
 // One workgroup's share of the stream-K attention: workgroup `wg` of `W`,
 // head_dim HD; `smem` is attn_streamk_lds<NW, HD>() bytes of LDS, 16-byte aligned.
-template <int GP, int NW, int D, int HD>
+template <int GP, int NW, int D, int HD, bool kSignal = false>
 __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, long W, char* smem) {
   constexpr int NT = NW * kWave;
   constexpr int kStageBytes = Dims<HD>::kStageBytes;
@@ -46,7 +56,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   constexpr int kWaveOut = GP * HD * 4;     // a wave's un-normalised output in its stage
   static_assert(kWaveOut + 2 * GP * 4 <= kStageBytes, "a wave's output fits its stage");
   static_assert(NT * 24 <= kStageBytes && NT * 4 <= kStageBytes, "merge scratch fits one stage");
-  int* const s_pre = reinterpret_cast<int*>(smem);  // blocks of the sequences before batch b (per kv head)
+  int* const s_pre = reinterpret_cast<int*>(smem);  // virtual blocks of the sequences before batch b (per kv head)
   int* const s_len = s_pre + kMaxAttnBatch + 1;
   char* const s_stage = smem + kAttnTableBytes;
   int* const s_scan = reinterpret_cast<int*>(s_stage);
@@ -60,9 +70,10 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int col = lane & 15, grp = lane >> 4;
   const int B = p.B, Hkv = p.Hkv, G = p.G;
+  const int cost = p.seq_cost;
   DA_TRACE(0);
 
-  // ---- blocks per sequence and their prefix sums (one scan per workgroup) ----
+  // ---- virtual blocks per sequence and their prefix sums (one scan per workgroup) ----
   const int per = (B + NT - 1) / NT;
   int local = 0;
   for (int j = 0; j < per; ++j) {
@@ -70,7 +81,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
     if (b < B) {
       const int L = min(max(p.seq_lens[b], 0), p.Lmax);
       s_len[b] = L;
-      local += (L + kBlockKeys - 1) / kBlockKeys;
+      local += (L + kBlockKeys - 1) / kBlockKeys + cost;
     }
   }
   s_scan[t] = local;
@@ -87,7 +98,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
       const int b = t * per + j;
       if (b < B) {
         s_pre[b] = run;
-        run += (s_len[b] + kBlockKeys - 1) / kBlockKeys;
+        run += (s_len[b] + kBlockKeys - 1) / kBlockKeys + cost;
       }
     }
     if (t == 0) s_pre[B] = s_scan[NT - 1];
@@ -104,18 +115,33 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   const long xe = range_bound(wg + 1, T, W);
   const rsrc_t part_o = make_rsrc(p.part_o, p.part_o_bytes);
   const rsrc_t part_ml = make_rsrc(p.part_ml, p.part_ml_bytes);
-  // the bf16 output of 4 dims
+  const rsrc_t flat_r = make_rsrc(p.flat, (uint32_t)min((size_t)p.B * p.Hq * HD * 2, (size_t)0xffffffffu));
+  // the bf16 output of 4 dims (device-coherent when a projection in the same grid reads it)
   auto store4 = [&](int b, int qh, int d4, const float (&o)[4], float inv) {
     const uint32_t w01 = (uint32_t)f32_to_bf16_rne(o[0] * inv) | ((uint32_t)f32_to_bf16_rne(o[1] * inv) << 16);
     const uint32_t w23 = (uint32_t)f32_to_bf16_rne(o[2] * inv) | ((uint32_t)f32_to_bf16_rne(o[3] * inv) << 16);
-    *reinterpret_cast<uint2*>(p.flat + ((size_t)b * p.Hq + qh) * HD + d4 * 4) = make_uint2(w01, w23);
+    const size_t e = ((size_t)b * p.Hq + qh) * HD + d4 * 4;
+    if constexpr (kSignal)
+      rsrc_st8_coherent(flat_r, (uint32_t)(e * 2), make_uint2(w01, w23));
+    else
+      *reinterpret_cast<uint2*>(p.flat + e) = make_uint2(w01, w23);
+  };
+  // a sequence's output is complete: count it in its kv head's ready counter
+  auto signal_ready = [&](int h) {
+    if constexpr (kSignal) {
+      wait_stores_done();
+      __syncthreads();
+      if (t < kStepReplicas)
+        __hip_atomic_fetch_add(&p.head_ready[(h * kStepReplicas + t) * kCounterStride], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
   };
 
-  // ---- the piece that starts at block y: its sequence (b, h) and block range ----
+  // ---- the sequence whose virtual blocks hold position y, and this range's piece of it ----
   struct Piece {
-    int b, h, seg, L;
-    int lb0, lb1;     // blocks [lb0, lb1) of the sequence
-    long ss, se, pe;  // the sequence's first and end block, the piece's end block (flattened)
+    int b, h, seg, L, nb;
+    int lb0, lb1;     // real blocks [lb0, lb1) of the sequence (empty if lb0 >= lb1)
+    long rs, se;      // the sequence's first real block and end block (virtual positions)
     bool whole;
   };
   auto piece_at = [&](long y) {
@@ -127,15 +153,16 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
     }
     pc.b = lo;
     const int pre_b = uniform(s_pre[pc.b]);
-    const int nb = uniform(s_pre[pc.b + 1]) - pre_b;
+    const int vb = uniform(s_pre[pc.b + 1]) - pre_b;
     const long seg0 = (long)Hkv * pre_b;
-    pc.h = (int)((y - seg0) / nb);
-    pc.ss = seg0 + (long)pc.h * nb;
-    pc.se = pc.ss + nb;
-    pc.pe = min(xe, pc.se);
-    pc.lb0 = (int)(y - pc.ss);
-    pc.lb1 = (int)(pc.pe - pc.ss);
-    pc.whole = (y == pc.ss && pc.pe == pc.se);
+    pc.h = (int)((y - seg0) / vb);
+    const long vs = seg0 + (long)pc.h * vb;
+    pc.rs = vs + cost;
+    pc.se = vs + vb;
+    pc.nb = vb - cost;
+    pc.lb0 = (int)(max(y, pc.rs) - pc.rs);
+    pc.lb1 = (int)(min(xe, pc.se) - pc.rs);
+    pc.whole = (pc.lb0 == 0 && pc.lb1 == pc.nb);
     pc.seg = pc.b * Hkv + pc.h;
     pc.L = uniform(s_len[pc.b]);
     return pc;
@@ -200,10 +227,12 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
       }
     }
 
-    if (!pc.whole) {
+    if (pc.whole) {
+      signal_ready(h);
+    } else {
       // (the barrier inside arrive_last_coherent also ends the reads of the waves' outputs,
       // whose bytes the merge scratch reuses)
-      const long first = range_owner(pc.ss, T, W), last = range_owner(pc.se - 1, T, W);
+      const long first = range_owner(pc.rs, T, W), last = range_owner(pc.se - 1, T, W);
       const int P = (int)(last - first + 1);
       const bool last_piece = arrive_last_coherent(&p.counters[seg], (uint32_t)P);
       DA_TRACE(3);
@@ -256,6 +285,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
           }
           __syncthreads();
         }
+        signal_ready(h);
         DA_TRACE(4);
       }
     }
@@ -264,15 +294,17 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
 
   while (x < xe) {
     const Piece pc = piece_at(x);
-    const AttnSeg sg = seg_of(pc);
-    uint4 qa[HD / 32];
-    query_of(qa, pc);
-    AttnWaveT<HD> aw;
-    aw.reset();
-    attn_wave_steps<GP, D, HD>(aw, qa, sg, pc.lb0 + wave, NW, wave_steps(pc), pc.L, s_stage + wave * kStageBytes,
-                               lane);
-    finish_piece(pc, aw);
-    x = pc.pe;
+    if (pc.lb0 < pc.lb1) {
+      const AttnSeg sg = seg_of(pc);
+      uint4 qa[HD / 32];
+      query_of(qa, pc);
+      AttnWaveT<HD> aw;
+      aw.reset();
+      attn_wave_steps<GP, D, HD>(aw, qa, sg, pc.lb0 + wave, NW, wave_steps(pc), pc.L, s_stage + wave * kStageBytes,
+                                 lane);
+      finish_piece(pc, aw);
+    }
+    x = min(xe, pc.se);
   }
   DA_TRACE(6);
 }

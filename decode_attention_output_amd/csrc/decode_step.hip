@@ -332,6 +332,7 @@ __device__ __forceinline__ void projection(const StepParams& p, int r, char* sme
 template <int GP, int MB, int TC>
 __global__ __launch_bounds__(kThreads, 2) void decode_step_kernel(StepParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kAttnLds];
+  DA_TRACE(14);
   if ((int)blockIdx.x < p.attn_wgs) {
     piece_attention<GP>(p, (int)blockIdx.x, smem);
     return;

@@ -32,12 +32,14 @@ struct AttnParams {
   float* part_ml;           // fp32 [slots, G, 2]   (max in log2 units, weight sum)
   uint32_t part_o_bytes, part_ml_bytes;
   uint32_t* counters;       // [B * Hkv] arrival counters, zero between calls
+  uint32_t* head_ready;     // single-launch large step: finished sequences per kv head (kStepReplicas copies)
   float* dbg_scores;        // optional fp32 [B, Hq, Lmax]
   float* dbg_lse;           // optional fp32 [B, Hq]
   int B, Hq, Hkv, G, Lmax;
   int head_dim;             // 128 or 256
   int num_workgroups;       // stream-K workgroups; slots = num_workgroups + B * Hkv
   int step_variant;         // 32-key steps in flight per wave: 0 = default (1), else 1..3
+  int seq_cost;             // virtual 32-key blocks a workgroup is charged for starting a sequence
   float scale;       // softmax scale (natural units)
   float scale_log2;  // scale * log2(e)
 };
@@ -70,6 +72,8 @@ struct GemmParams {
 };
 constexpr int kGemmTileN = 128;   // output columns per GEMM workgroup
 constexpr int kGemmDepth = 2;     // 32-row steps per wave in flight while one is multiplied
+constexpr int kGemmDepthWait = 4;  // the same in the single-launch large step, whose items request
+                                   // that many steps before they wait for the attention
 
 hipError_t launch_attention(const AttnParams& p, int gpad, hipStream_t s);
 // The single-launch decode step for small steps (a few tokens, a few thousand
@@ -111,6 +115,41 @@ constexpr int kStepReplicas = 4;
 constexpr int kStepCounterBase = kMaxCounters - 64;  // pass_top, error, then pass_sub[32] at +32
 constexpr int kStepErrorWord = kStepCounterBase + 1;  // the error word, read back by decode_attn_step_status
 constexpr uint32_t kStepWaitPolls = 1u << 20;         // default bound of a projection workgroup's wait
+
+// Hand-over from the attention to the projection workgroups of a
+// single-launch step (step_sync.hpp): per-kv-head ready counters, kept
+// kStepReplicas times one per line, and the count of workgroups past their wait.
+struct ReadySync {
+  uint32_t* ready;      // [heads * kStepReplicas] copies, kCounterStride words apart
+  uint32_t* pass_sub;   // [32] workgroups past their wait, by index mod 32
+  uint32_t* pass_top;   // groups of pass_sub that are complete
+  uint32_t* error;      // set to 1 when a wait gave up
+  int heads;            // kv heads
+  uint32_t target;      // a head is ready when its counter reaches this
+  uint32_t wait_polls;  // polls of one counter before giving up (>= 1)
+  int waiters;          // workgroups that wait
+};
+
+// What a GEMM item of the single-launch large step waits for: the ready
+// counters of the kv heads whose query heads (head_dim rows of K each, `group`
+// query heads per kv head) make up its K-chunk; `waiter` is its index among the
+// waiting workgroups.
+struct GemmWait {
+  ReadySync sync;
+  int head_dim, group;
+  int waiter;
+};
+
+// The single-launch large step: stream-K attention workgroups, then one
+// workgroup per MFMA GEMM item (ntiles column tiles x mgroups row groups x
+// gemm.ksplit K-chunks, K-chunk major).
+struct StepLargeParams {
+  AttnParams attn;
+  GemmParams gemm;
+  GemmWait wait;
+  int ntiles, mgroups;
+};
+hipError_t launch_decode_step_large(const StepLargeParams& p, int gpad, hipStream_t s);
 
 // Shapes the single-launch step is built for: query group (padded), batch rows
 // (padded) and tile_n output columns per projection workgroup, whose K-chunk

@@ -85,9 +85,13 @@ extern "C" {
  *                   every chunk is a whole number of the kernel's row batches)
  *  step_mode        0 built-in, 1 one launch where the single-launch step
  *                   supports the shape, 2 two launches (as DA_FLAG_SEPARATE)
- *  step_wait_polls  bound of the single-launch step's waits, in polls of a
+ *  step_wait_polls  bound of the single-launch steps' waits, in polls of a
  *                   counter, 1..2^24 (built-in 2^20, a fraction of a second);
  *                   a workgroup that reaches it gives up (decode_attn_step_status)
+ *  attn_seq_cost    stream-K attention: 32-key blocks of work a workgroup is
+ *                   charged for each sequence it starts, 1..256 (built-in 6),
+ *                   so that workgroups whose range crosses sequence boundaries
+ *                   get fewer keys
  */
 typedef struct {
   int32_t attn_workgroups;
@@ -96,6 +100,7 @@ typedef struct {
   int32_t proj_ksplit;
   int32_t step_mode;
   int32_t step_wait_polls;
+  int32_t attn_seq_cost;
 } decode_attn_tiles_t;
 
 /*
@@ -163,8 +168,13 @@ typedef struct {
   int32_t num_splits;   /* ceil(max_seq_len / split_len)                              */
   int32_t oproj_path;   /* 0: VALU GEMV, 1: MFMA GEMM (two-launch projection)        */
   int32_t fused;        /* 1: decode_attn_fwd runs the step as one launch (small
-                           steps, B < 16): projection workgroups stream their weight
-                           tile while the attention runs, then wait for it          */
+                           steps, B <= 4): projection workgroups stream their weight
+                           tile while the attention runs, then wait for it;
+                           2: one launch for larger steps (head_dim 128, B <= 32):
+                           the stream-K attention workgroups, then the MFMA
+                           projection's items, each of which requests its first
+                           weight rows and waits for the kv heads of its K-chunk;
+                           0: two launches                                         */
   size_t workspace_bytes;
 } decode_attn_plan_t;
 

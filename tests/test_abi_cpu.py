@@ -171,7 +171,7 @@ def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
     # the long axis (keys) is streamed 32 keys per wave step and cut evenly over the workgroups
     assert plan.qk.tile_n == 32 and plan.pv.tile_k == 32
     keys = cfg["batch"] * cfg["num_kv_heads"] * cfg["max_seq_len"]
-    if plan.fused:
+    if plan.fused == 1:
         # one launch: every sequence cut into the same pieces of a multiple of 128 keys
         assert plan.split_len % 128 == 0 and plan.num_splits == -(-cfg["max_seq_len"] // plan.split_len)
         assert plan.qk.workgroups == cfg["batch"] * cfg["num_kv_heads"] * plan.num_splits
@@ -186,9 +186,9 @@ def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
         assert plan.qk.workgroups >= min(192, keys // 128)
         assert plan.split_len >= min(128, 32 * (-(-keys // 32)))
         assert plan.oproj.workgroups >= min(256, (cfg["hidden"] // 128) * (cfg["num_q_heads"] * 128 // 128))
-    # projection path: the single-launch step's own VALU projection, else the MFMA GEMM at
-    # every batch (K = Hq*128)
-    assert plan.oproj_path == (0 if plan.fused else 1)
+    # projection path: the small single-launch step's own VALU projection, else the MFMA GEMM at
+    # every batch (K = Hq*128), in the large single-launch step (fused 2) or a launch of its own
+    assert plan.oproj_path == (0 if plan.fused == 1 else 1)
     assert plan.workspace_bytes == da.decode_attn_workspace_size(da.make_shape(**cfg))
 
 
@@ -200,16 +200,21 @@ LARGE = [dict(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=8192, hidden
 
 
 @pytest.mark.parametrize("cfg", SMALL + LARGE)
-def test_plan_fuses_small_steps_only(lib, cfg):
+def test_plan_one_launch_per_step(lib, cfg):
+    # small steps: the single-launch step with its own projection (fused 1); larger ones: the
+    # stream-K attention and the MFMA projection's items in one grid (fused 2)
     plan = da.decode_attn_plan(da.make_shape(**cfg))
     sep = da.decode_attn_plan(da.make_shape(flags=da.DA_FLAG_SEPARATE, **cfg))
-    assert plan.fused == (1 if cfg in SMALL else 0)
+    assert plan.fused == (1 if cfg in SMALL else 2)
     assert sep.fused == 0
     # the workspace does not depend on the launch choice
     assert plan.workspace_bytes == sep.workspace_bytes
-    if not plan.fused:
-        assert (sep.qk.workgroups, sep.split_len) == (plan.qk.workgroups, plan.split_len)
-    if plan.fused:
+    if plan.fused == 2:
+        # the same attention split and projection tiles as two launches
+        for name in ("qk", "pv", "oproj"):
+            assert getattr(sep, name).as_dict() == getattr(plan, name).as_dict(), name
+        assert sep.split_len == plan.split_len
+    if plan.fused == 1:
         # every workgroup of the single launch is resident at once (two per compute unit)
         assert plan.qk.workgroups + plan.oproj.workgroups <= 512
         assert plan.oproj_path == 0 and plan.oproj.tile_n in (128, 256, 512)
@@ -218,7 +223,8 @@ def test_plan_fuses_small_steps_only(lib, cfg):
 @pytest.mark.parametrize("tiles", [dict(attn_workgroups=-1), dict(attn_workgroups=1025), dict(attn_depth=4),
                                    dict(attn_depth=-2), dict(proj_tile_n=96), dict(proj_tile_n=1024),
                                    dict(proj_ksplit=-1), dict(step_mode=3), dict(step_wait_polls=-1),
-                                   dict(step_wait_polls=(1 << 24) + 1)])
+                                   dict(step_wait_polls=(1 << 24) + 1), dict(attn_seq_cost=-1),
+                                   dict(attn_seq_cost=257)])
 def test_tile_override_out_of_range_is_a_shape_error(lib, tiles):
     shape = _shape(tiles=tiles)
     assert da.decode_attn_workspace_size(shape) == 0

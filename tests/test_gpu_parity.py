@@ -453,3 +453,54 @@ def test_single_launch_step_timeout_is_reported(gpu):
     _status_ok(ws, "after the counters were zero-filled")
     _counter_block_is_clear(ws)
     _check_step(inp, {"flat": flat, "out": out}, what="after a timeout")
+
+
+# ---- the single-launch large step against two launches -----------------------
+
+LARGE = [
+    # (batch, Hq, Hkv, seq_lens, max_seq_len, hidden)
+    (5, 32, 8, [3000, 17, 2048, 999, 64], 3000, 4096),
+    (16, 32, 8, [1024 + 431 * i for i in range(16)], 8192, 4096),
+    (6, 16, 2, [1, 33, 700, 129, 5000, 2], 5000, 264),      # sequences shorter than a stream-K range
+    (32, 8, 1, [64 + 97 * i for i in range(32)], 3200, 512),   # two 16-row m-tiles, one kv head
+    (4, 64, 8, [2000, 2001, 4095, 4096], 4096, 8192),          # group 8, 8 K-chunks of 1024 rows
+]
+
+
+@pytest.mark.parametrize("case", LARGE, ids=lambda c: "B%d_H%d_KV%d_Lmax%d_N%d" % (c[0], c[1], c[2], c[4], c[5]))
+def test_single_launch_large_step_matches_the_oracle_and_two_launches(gpu, case):
+    B, Hq, Hkv, sl, Lmax, hidden = case
+    assert da.decode_attn_plan(da.make_shape(B, Hq, Hkv, Lmax, hidden)).fused == 2
+    inp = workloads.custom_decode_inputs(B, Hq, Hkv, sl, max_seq_len=Lmax, hidden=hidden, seed=B * 100 + Hq + hidden)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    s, w = dev_i32(inp["seq_lens"]), dev_bf16(inp["o_weight"])
+    ws = PoisonedWorkspace()
+    flat = host_words(da.decode_attn_only(q, k, v, s, workspace=ws))
+    outs = []
+    for separate in (False, True, False):
+        outs.append(host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, separate=separate)))
+        _status_ok(ws, "large single launch")
+        _counter_block_is_clear(ws)
+    _check_step(inp, {"flat": flat, "out": outs[0]}, what="large single launch")
+    # the same kernels' arithmetic in one launch or two: the same bits, and deterministic
+    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], outs[2])
+
+
+def test_single_launch_large_step_timeout_is_reported(gpu):
+    # projection workgroups allowed one poll give up while the attention of 16 x 8192 keys still runs
+    B, Hq, Hkv, L, hidden = 16, 32, 8, 8192, 4096
+    assert da.decode_attn_plan(da.make_shape(B, Hq, Hkv, L, hidden)).fused == 2
+    inp = workloads.custom_decode_inputs(B, Hq, Hkv, [L] * B, max_seq_len=L, hidden=hidden, seed=72)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    s, w = dev_i32(inp["seq_lens"]), dev_bf16(inp["o_weight"])
+    ws = PoisonedWorkspace()
+    flat = host_words(da.decode_attn_only(q, k, v, s, workspace=ws))
+    out = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, tiles=dict(step_wait_polls=1)))
+    assert da.decode_attn_step_status(ws) == da.DA_ERR_TIMEOUT
+    assert np.isnan(bf16_words_to_f64(out)).any(), "a workgroup gave up but no output is NaN"
+    ws.buf[:COUNTER_BLOCK].zero_()
+    out = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws))
+    _status_ok(ws, "after the counters were zero-filled")
+    _counter_block_is_clear(ws)
+    _check_step(inp, {"flat": flat, "out": out}, what="large step after a timeout")

@@ -16,8 +16,9 @@ from gpu_helpers import PoisonedWorkspace, assert_bf16_close, dev_bf16, dev_i32,
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (batch, Hq, Hkv, seq_lens, max_seq_len, hidden): two launches (stream-K attention, MFMA
-    # projection), then a smaller step that runs as one launch
+    # (batch, Hq, Hkv, seq_lens, max_seq_len, hidden): the large single-launch step (stream-K
+    # attention and the MFMA projection's items in one grid), then a smaller step that runs as the
+    # small single-launch step
     (6, 32, 8, [3000, 40, 2048, 999, 64, 2500], 3000, 4096),
     (1, 8, 2, [300], 300, 512),
 ]
@@ -35,7 +36,7 @@ def _noalloc(q, k, v, s, w, out):
 
 def test_noalloc_matches_decode_attn_fwd_twice(gpu):
     plans = [da.decode_attn_plan(da.make_shape(c[0], c[1], c[2], c[4], c[5])).fused for c in CASES]
-    assert plans == [0, 1]
+    assert plans == [2, 1]
     for i, (B, Hq, Hkv, sl, Lmax, hidden) in enumerate(CASES):
         inp = workloads.custom_decode_inputs(B, Hq, Hkv, sl, max_seq_len=Lmax, hidden=hidden, seed=900 + i)
         q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
