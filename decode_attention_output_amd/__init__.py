@@ -56,7 +56,8 @@ EXPORTED = (
 class DecodeAttnTiles(ctypes.Structure):
     """Tile override of one call (decode_attn_tiles_t); zero fields keep the built-in choice."""
     _fields_ = [(n, ctypes.c_int32) for n in ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit",
-                                              "step_mode", "step_wait_polls", "attn_seq_cost")]
+                                              "step_mode", "step_wait_polls", "attn_seq_cost",
+                                              "step_weight_delay")]
 
 
 def make_tiles(tiles) -> Optional[DecodeAttnTiles]:

@@ -86,6 +86,7 @@ bool tiles_ok(const decode_attn_shape_t* s) {
   if (t->proj_ksplit < 0 || t->step_mode < 0 || t->step_mode > 2) return false;
   if (t->step_wait_polls < 0 || t->step_wait_polls > (1 << 24)) return false;
   if (t->attn_seq_cost < 0 || t->attn_seq_cost > kMaxAttnSeqCost) return false;
+  if (t->step_weight_delay < 0 || t->step_weight_delay > 1000) return false;
   if (const int tn = t->proj_tile_n) {
     if (tn != 64 && tn != 128 && tn != 256 && tn != 512) return false;
     // 128 is the MFMA GEMM's tile; the other widths ask for the GEMV (batch < 16)
@@ -216,7 +217,7 @@ AttnPlan plan_attn(const decode_attn_shape_t* s) {
 // every dependent trip through memory then outweighs the streaming time.
 constexpr size_t kStepMaxKvBytes = 64ull << 20;
 constexpr size_t kStepMaxWeightBytes = 64ull << 20;
-constexpr int kStepMaxBatch = 4;          // projection rows held per lane
+constexpr int kStepMaxBatch = 2;          // projection rows held per lane (four spill registers)
 constexpr int kStepResident = 512;        // workgroups resident at once: two 256-thread ones per CU
 constexpr int kStepAttnTarget = 128;      // attention workgroups aimed at
 constexpr int kStepMaxAttn = 384;         // at most, leaving room for the projection
@@ -273,7 +274,8 @@ StepPlan plan_step(const decode_attn_shape_t* s) {
   sp.part_o_bytes = align_up((size_t)sp.attn_wgs * G * kHeadDim * sizeof(float), kAlign);
   sp.part_ml_bytes = align_up((size_t)sp.attn_wgs * G * 2 * sizeof(float), kAlign);
   sp.proj_part_bytes = sp.chunks > 1 ? align_up((size_t)sp.chunks * B * N * sizeof(float), kAlign) : 0;
-  sp.ok = (seqs * da::kStepReplicas + sp.tiles) * da::kCounterStride <= da::kStepCounterBase;
+  // counters, one per line: ready copies per kv head, K-chunks per column tile
+  sp.ok = (Hkv * da::kStepReplicas + sp.tiles) * da::kCounterStride <= da::kStepCounterBase;
   return sp;
 }
 
@@ -450,11 +452,16 @@ int run_step(const void* q, const void* k, const void* v, const int32_t* sl, con
   p.part_o_bytes = (uint32_t)sp.part_o_bytes;
   p.part_ml_bytes = (uint32_t)sp.part_ml_bytes;
   p.proj_part_bytes = (uint32_t)sp.proj_part_bytes;
-  p.seq_cnt = cnt;
-  p.proj_cnt = cnt + s->batch * s->num_kv_heads * da::kStepReplicas * da::kCounterStride;
-  p.pass_top = cnt + da::kStepCounterBase;
-  p.error = cnt + da::kStepErrorWord;
-  p.pass_sub = cnt + da::kStepCounterBase + 32;
+  da::ReadySync& r = p.sync;
+  r.ready = cnt;
+  r.pass_top = cnt + da::kStepCounterBase;
+  r.error = cnt + da::kStepErrorWord;
+  r.pass_sub = cnt + da::kStepCounterBase + 32;
+  r.heads = s->num_kv_heads;
+  r.target = (uint32_t)(s->batch * sp.pieces);  // pieces of every sequence of the kv head
+  r.wait_polls = s->tiles && s->tiles->step_wait_polls ? (uint32_t)s->tiles->step_wait_polls : da::kStepWaitPolls;
+  r.waiters = sp.tiles * sp.chunks;
+  p.proj_cnt = r.ready + s->num_kv_heads * da::kStepReplicas * da::kCounterStride;
   p.B = s->batch;
   p.Hq = s->num_q_heads;
   p.Hkv = s->num_kv_heads;
@@ -466,7 +473,7 @@ int run_step(const void* q, const void* k, const void* v, const int32_t* sl, con
   p.attn_wgs = sp.attn_wgs;
   p.tiles = sp.tiles;
   p.chunks = sp.chunks;
-  p.wait_polls = s->tiles && s->tiles->step_wait_polls ? (uint32_t)s->tiles->step_wait_polls : da::kStepWaitPolls;
+  p.weight_delay = s->tiles ? (uint32_t)s->tiles->step_weight_delay : 0u;
   const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
   p.scale_log2 = scale * 1.4426950408889634f;
   return da::launch_decode_step(p, sp.gpad, sp.mpad, sp.tile_n, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;

@@ -9,7 +9,8 @@
 //    into `pieces` fixed pieces of piece_keys keys (the last ones may be short
 //    or empty); a workgroup computes one piece for the G query heads of the
 //    group, stores its un-normalised output, running max and weight sum
-//    through device-coherent stores, and counts the piece in seq_cnt.
+//    through device-coherent stores, and counts the piece in its kv head's
+//    ready counter (step_sync.hpp).
 //  - the rest: projection. A workgroup owns TC output columns of one K-chunk
 //    of the weight, the rows of whole kv heads. It first issues the loads of
 //    its whole weight tile (held in registers), so the weight streams from
@@ -22,12 +23,11 @@
 // memory, and no workgroup waits for heads it does not use.
 // Workgroups are dispatched in index order, so every attention workgroup is
 // running before a projection workgroup waits; the waits are bounded (a
-// workgroup that gives up sets `error` and writes NaN). The last projection
-// workgroup to pass its wait, counted in two levels (32 counters, then one) so
-// that no single address takes more than a few dozen atomics, checks that
-// every piece has been counted and returns seq_cnt to zero.
+// workgroup that gives up sets the error word and writes NaN), and the last
+// projection workgroup past its wait returns the ready counters to zero.
 #include "attn_core.hpp"
 #include "gemv_core.hpp"
+#include "step_sync.hpp"
 
 namespace da {
 
@@ -35,7 +35,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kPassGroups = 32;
 constexpr int kMergeLoads = 8;             // pieces whose loads are in flight together in the merge
 constexpr int kRowsPerLane = 32;           // weight rows a projection lane holds (16 bytes each)
 constexpr uint32_t kNoLoad = 0x80000000u;  // buffer offset past every range: the load returns 0, no request
@@ -124,7 +123,7 @@ __device__ __forceinline__ void piece_attention(const StepParams& p, int a, char
   wait_stores_done();
   __syncthreads();
   if (t < kStepReplicas)
-    __hip_atomic_fetch_add(&p.seq_cnt[(seq * kStepReplicas + t) * kCounterStride], 1u, __ATOMIC_RELAXED,
+    __hip_atomic_fetch_add(&p.sync.ready[(h * kStepReplicas + t) * kCounterStride], 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   DA_TRACE(3);
 }
@@ -155,77 +154,29 @@ __device__ __forceinline__ void projection(const StepParams& p, int r, char* sme
   // order, so the wave that polls below (wave 0) waits only for its own rows.
   uint4 wv[UR];
   const uint16_t* wrow = p.w + (size_t)(chunk * KC + rr) * p.N + n;
+  if (p.weight_delay) {
+    // requested weight_delay ticks (100 MHz) after the workgroup starts, so that the
+    // attention's K/V requests, issued first, are not queued behind the weight
+    const uint64_t t0 = wall_clock64();
+    while (wall_clock64() - t0 < p.weight_delay) __builtin_amdgcn_s_sleep(4);
+  }
 #pragma unroll
   for (int u = 0; u < UR; ++u) wv[u] = n < p.N ? ld16(wrow + (size_t)u * RPP * p.N) : make_uint4(0, 0, 0, 0);
 
-  // wait until every piece of the chunk's kv heads (all batch rows) is stored.
-  // The wait is bounded: a workgroup that gives up sets the error word, which
-  // the host reads back (decode_attn_step_status), and its output tile becomes
-  // NaN so that the failure cannot pass for a result.
-  __shared__ uint32_t s_flags;  // bit 0: this workgroup gave up; bit 1: it clears the piece counters
+  // wait until every piece of the chunk's kv heads (all batch rows) is stored;
+  // a workgroup that gives up writes NaN, so that the failure cannot pass for a
+  // result (step_sync.hpp)
+  // The count of workgroups past their wait is settled after the multiply, so
+  // that its atomics' round trips overlap the merge.
+  __shared__ uint32_t s_flag;
+  uint32_t prev_pass = 0;
   const int qh0 = chunk * NH;
-  const int h0 = qh0 / p.G, nkv = (qh0 + NH - 1) / p.G - h0 + 1;
   if (t == 0) {
-    uint32_t polls = 0;
-    bool ok = true;
-    for (int m = 0; m < p.B && ok; ++m)
-      for (int hh = 0; hh < nkv && ok; ++hh) {
-        const uint32_t* c = &p.seq_cnt[((m * p.Hkv + h0 + hh) * kStepReplicas + r % kStepReplicas) * kCounterStride];
-        while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.pieces) {
-          if (++polls >= p.wait_polls) {
-            ok = false;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(8);
-        }
-      }
-    if (!ok) {
-      __hip_atomic_store(p.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_stores_done();  // the error word is in place before this workgroup counts itself past the wait
-    }
-    // count this workgroup past its wait; the last one clears the piece counters
-    uint32_t flags = ok ? 0u : 1u;
-    const int P = (int)gridDim.x - p.attn_wgs;
-    const int g = r % kPassGroups;
-    const uint32_t in_group = (uint32_t)(P / kPassGroups + (g < P % kPassGroups ? 1 : 0));
-    if (__hip_atomic_fetch_add(&p.pass_sub[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_group - 1) {
-      __hip_atomic_store(&p.pass_sub[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t ngroups = (uint32_t)min(P, kPassGroups);
-      if (__hip_atomic_fetch_add(p.pass_top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1) {
-        __hip_atomic_store(p.pass_top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        flags |= 2u;
-      }
-    }
-    s_flags = flags;
+    s_flag = ready_wait(p.sync, qh0 / p.G, (qh0 + NH - 1) / p.G, r % kStepReplicas) ? 0u : 1u;
+    prev_pass = ready_pass_sub(p.sync, r);
   }
   __syncthreads();
-  if (s_flags & 2u) {
-    // Every workgroup is past its wait. Before the piece counters return to
-    // zero, every copy of every sequence's counter must be complete: a copy
-    // that no workgroup polled may still have an increment in flight. If a
-    // copy stays short (some workgroup gave up), the counters stay as they
-    // are and the error word is set; the caller zero-fills them again.
-    const int ncnt = p.B * p.Hkv * kStepReplicas;
-    bool done = __hip_atomic_load(p.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
-    for (int i = t; i < ncnt && done; i += kThreads) {
-      const uint32_t* c = &p.seq_cnt[i * kCounterStride];
-      uint32_t polls = 0;
-      while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.pieces) {
-        if (++polls >= p.wait_polls) {
-          done = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-      }
-    }
-    done = __syncthreads_and(done);
-    if (done) {
-      for (int i = t; i < ncnt; i += kThreads)
-        __hip_atomic_store(&p.seq_cnt[i * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (t == 0) {
-      __hip_atomic_store(p.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  const bool gave_up = s_flag != 0;
   DA_TRACE(9);
 
   // merge the pieces of the chunk's heads: (batch row, head, 4 dims) per lane,
@@ -308,7 +259,12 @@ __device__ __forceinline__ void projection(const StepParams& p, int r, char* sme
     }
   }
   DA_TRACE(11);
-  if (s_flags & 1u) {
+  // the last workgroup past its wait returns the ready counters to zero
+  __syncthreads();  // every thread has read s_flag
+  if (t == 0) s_flag = ready_pass_last(p.sync, r, prev_pass) ? 1u : 0u;
+  __syncthreads();
+  ready_clear(p.sync, s_flag != 0);
+  if (gave_up) {
 #pragma unroll
     for (int mm = 0; mm < MB; ++mm)
 #pragma unroll
@@ -361,7 +317,6 @@ hipError_t launch_step_gp(const StepParams& p, int mpad, int tile_n, hipStream_t
   switch (mpad) {
     case 1: return launch_step_mb<GP, 1>(p, tile_n, s);
     case 2: return launch_step_mb<GP, 2>(p, tile_n, s);
-    case 4: return launch_step_mb<GP, 4>(p, tile_n, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -370,7 +325,7 @@ hipError_t launch_step_gp(const StepParams& p, int mpad, int tile_n, hipStream_t
 
 bool decode_step_supported(int gpad, int mpad, int tile_n) {
   const bool g_ok = gpad == 1 || gpad == 2 || gpad == 4 || gpad == 8;
-  const bool m_ok = mpad == 1 || mpad == 2 || mpad == 4;
+  const bool m_ok = mpad == 1 || mpad == 2;
   const bool t_ok = tile_n == 128 || tile_n == 256 || tile_n == 512;
   return g_ok && m_ok && t_ok;
 }

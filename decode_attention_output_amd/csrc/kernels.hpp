@@ -76,38 +76,15 @@ constexpr int kGemmDepthWait = 4;  // the same in the single-launch large step, 
                                    // that many steps before they wait for the attention
 
 hipError_t launch_attention(const AttnParams& p, int gpad, hipStream_t s);
-// The single-launch decode step for small steps (a few tokens, a few thousand
-// cached keys): attention workgroups, one per fixed piece of every (batch, kv
-// head) sequence, followed in the same grid by projection workgroups that
-// merge the pieces of the heads they need and multiply.
-struct StepParams {
-  const uint16_t* q;        // bf16 [B, Hq, 128]
-  const uint16_t* k;        // bf16 [B, Hkv, Lmax, 128]
-  const uint16_t* v;        // bf16 [B, Hkv, Lmax, 128]
-  const int32_t* seq_lens;  // [B]
-  const uint16_t* w;        // bf16 [Hq*128, N]
-  uint16_t* out;            // bf16 [B, N]
-  float* part_o;            // fp32 [B*Hkv*pieces, G, 128] un-normalised piece outputs
-  float* part_ml;           // fp32 [B*Hkv*pieces, G, 2]   (max in log2 units, weight sum)
-  float* proj_part;         // fp32 [chunks, B, N] (chunks > 1)
-  uint32_t part_o_bytes, part_ml_bytes, proj_part_bytes;
-  uint32_t* seq_cnt;        // pieces stored per sequence, kStepReplicas copies, one per 128-byte line
-  uint32_t* proj_cnt;       // arrival counters of the K-chunks per column tile (chunks > 1), one per line
-  uint32_t* pass_sub;       // [32] projection workgroups past their wait, by index mod 32
-  uint32_t* pass_top;       // groups of pass_sub that are complete
-  uint32_t* error;          // set to 1 when a projection workgroup stopped waiting (read by the host)
-  int B, Hq, Hkv, G, Lmax, N;
-  int piece_keys, pieces;   // keys per piece (a multiple of 128), pieces per sequence
-  int attn_wgs;             // B * Hkv * pieces
-  int tiles, chunks;        // projection: column tiles x K-chunks (query heads of one kv head or whole kv heads)
-  uint32_t wait_polls;      // polls of a counter before a projection workgroup gives up waiting (>= 1)
-  float scale_log2;         // softmax scale * log2(e)
-};
-
-// Counters of the single-launch step that many workgroups poll or update sit
-// one per 128-byte line (accesses to one line are serialised), and every
-// sequence's piece count is kept kStepReplicas times, so that each copy has
-// only a few pollers: seq_cnt[(seq * kStepReplicas + copy) * kCounterStride].
+// The single-launch decode step for small steps (a few tokens, a few
+// thousand cached keys): attention workgroups, one per fixed piece of every
+// (batch, kv head) sequence, followed in the same grid by projection
+// workgroups that wait for the pieces of the kv heads they need, merge them
+// and multiply.
+// Counters of the single-launch steps that many workgroups poll or update sit
+// one per 128-byte line (accesses to one line are serialised), and every kv
+// head's ready counter is kept kStepReplicas times, so that each copy has only
+// a few pollers: ready[(head * kStepReplicas + copy) * kCounterStride].
 constexpr int kCounterStride = 32;
 constexpr int kStepReplicas = 4;
 
@@ -138,6 +115,27 @@ struct GemmWait {
   ReadySync sync;
   int head_dim, group;
   int waiter;
+};
+
+struct StepParams {
+  const uint16_t* q;        // bf16 [B, Hq, 128]
+  const uint16_t* k;        // bf16 [B, Hkv, Lmax, 128]
+  const uint16_t* v;        // bf16 [B, Hkv, Lmax, 128]
+  const int32_t* seq_lens;  // [B]
+  const uint16_t* w;        // bf16 [Hq*128, N]
+  uint16_t* out;            // bf16 [B, N]
+  float* part_o;            // fp32 [B*Hkv*pieces, G, 128] un-normalised piece outputs
+  float* part_ml;           // fp32 [B*Hkv*pieces, G, 2]   (max in log2 units, weight sum)
+  float* proj_part;         // fp32 [chunks, B, N] (chunks > 1)
+  uint32_t part_o_bytes, part_ml_bytes, proj_part_bytes;
+  uint32_t* proj_cnt;       // arrival counters of the K-chunks per column tile (chunks > 1), one per line
+  ReadySync sync;           // stored pieces per kv head, the projection's wait and its pass count
+  int B, Hq, Hkv, G, Lmax, N;
+  int piece_keys, pieces;   // keys per piece (a multiple of 128), pieces per sequence
+  int attn_wgs;             // B * Hkv * pieces
+  int tiles, chunks;        // projection: column tiles x K-chunks (whole query heads)
+  uint32_t weight_delay;    // 100 MHz ticks between a projection workgroup's start and its weight requests
+  float scale_log2;         // softmax scale * log2(e)
 };
 
 // The single-launch large step: stream-K attention workgroups, then one

@@ -92,6 +92,10 @@ extern "C" {
  *                   charged for each sequence it starts, 1..256 (built-in 6),
  *                   so that workgroups whose range crosses sequence boundaries
  *                   get fewer keys
+ *  step_weight_delay small single-launch step: time between a projection
+ *                   workgroup's start and its weight requests, in 10 ns ticks,
+ *                   0..1000 (built-in 0), so that the attention's K/V requests
+ *                   are served ahead of the weight
  */
 typedef struct {
   int32_t attn_workgroups;
@@ -101,6 +105,7 @@ typedef struct {
   int32_t step_mode;
   int32_t step_wait_polls;
   int32_t attn_seq_cost;
+  int32_t step_weight_delay;
 } decode_attn_tiles_t;
 
 /*
@@ -168,7 +173,7 @@ typedef struct {
   int32_t num_splits;   /* ceil(max_seq_len / split_len)                              */
   int32_t oproj_path;   /* 0: VALU GEMV, 1: MFMA GEMM (two-launch projection)        */
   int32_t fused;        /* 1: decode_attn_fwd runs the step as one launch (small
-                           steps, B <= 4): projection workgroups stream their weight
+                           steps, B <= 2): projection workgroups stream their weight
                            tile while the attention runs, then wait for it;
                            2: one launch for larger steps (head_dim 128, B <= 32):
                            the stream-K attention workgroups, then the MFMA

@@ -194,8 +194,9 @@ def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
 
 SMALL = [dict(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=256, hidden=512),
          dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=2048, hidden=4096),
-         dict(batch=3, num_q_heads=16, num_kv_heads=2, max_seq_len=128, hidden=256)]
-LARGE = [dict(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=8192, hidden=4096),
+         dict(batch=2, num_q_heads=16, num_kv_heads=2, max_seq_len=128, hidden=256)]
+LARGE = [dict(batch=3, num_q_heads=16, num_kv_heads=2, max_seq_len=128, hidden=256),
+         dict(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=8192, hidden=4096),
          dict(batch=4, num_q_heads=64, num_kv_heads=8, max_seq_len=32768, hidden=8192)]
 
 

@@ -227,9 +227,8 @@ FUSED = [
     (1, 32, 8, [2048], 2048, 4096),
     (1, 8, 8, [1], 1, 128),
     (2, 2, 1, [16, 17], 17, 1032),
-    (3, 16, 2, [5, 37, 100], 128, 256),
-    (4, 8, 2, [255, 256, 257, 1000], 1024, 640),
-    (4, 32, 8, [1000, 17, 600, 999], 1000, 4096),
+    (2, 16, 2, [5, 100], 128, 256),
+    (2, 8, 1, [1000, 257], 1024, 640),
 ]
 
 
@@ -464,6 +463,9 @@ LARGE = [
     (6, 16, 2, [1, 33, 700, 129, 5000, 2], 5000, 264),      # sequences shorter than a stream-K range
     (32, 8, 1, [64 + 97 * i for i in range(32)], 3200, 512),   # two 16-row m-tiles, one kv head
     (4, 64, 8, [2000, 2001, 4095, 4096], 4096, 8192),          # group 8, 8 K-chunks of 1024 rows
+    (3, 16, 2, [5, 37, 100], 128, 256),                         # small steps of more than two sequences
+    (4, 8, 2, [255, 256, 257, 1000], 1024, 640),
+    (4, 32, 8, [1000, 17, 600, 999], 1000, 4096),
 ]
 
 
