@@ -102,8 +102,9 @@ def dominant_kernel(wl, plan, seq_lens):
         + 2 * s.batch * s.o_in
     proj_bytes = 2 * s.o_in * s.hidden + 2 * s.batch * s.o_in + 2 * s.batch * s.hidden
     if plan.fused:
-        # one launch carries the whole step
-        return "decode_step_kernel", workloads_alg_bytes(s, seq_lens), "step"
+        # one launch carries the whole step: the small single-launch step (1) or the large one (2)
+        name = "decode_step_kernel" if plan.fused == 1 else "decode_step_large_kernel"
+        return name, workloads_alg_bytes(s, seq_lens), "step"
     if proj_bytes >= attn_bytes:
         return ("gemv_kernel" if plan.oproj_path == 0 else "gemm_kernel"), proj_bytes, "oproj"
     return "attn_streamk_kernel", attn_bytes, "attention"
@@ -123,6 +124,55 @@ def repeat_and_warm(run_steps, steps, repeats=5):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     warm = run_steps(e0, e1, rotate=False) * 1e3 / steps
     return [round(x, 3) for x in res], round(statistics.median(res), 3), round(warm, 3)
+
+
+def stream_floor(nbytes, stream, min_rotate_mib, launches=200):
+    """The floor of a step of `nbytes`: the best time of a plain streaming read of that many bytes
+    (decode_attn_read_probe, the attention's 1 KiB-per-instruction load pattern) over rotated
+    buffers, back to back on the bench stream, for a few workgroup counts."""
+    import torch
+
+    import decode_attention_output_amd as da
+
+    lib = da.load_library()
+    nbytes = (nbytes + 15) // 16 * 16
+    R = max(1, math.ceil(min_rotate_mib * 2 ** 20 / nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    sink = torch.empty(65536, dtype=torch.int32, device="cuda")
+    best = None
+    for wgs in (256, 512, 1024, 2048):
+        def launch(i):
+            rc = lib.decode_attn_read_probe(bufs[i % R].data_ptr(), nbytes, sink.data_ptr(), wgs, stream.cuda_stream)
+            if rc != da.DA_OK:
+                raise da.DecodeAttnError(rc, "decode_attn_read_probe")
+        for i in range(50):
+            launch(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(launches):
+            launch(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        if best is None or us < best[0]:
+            best = (us, wgs)
+    del bufs
+    tbs = nbytes / (best[0] * 1e-6) / 1e12
+    return {"us": round(best[0], 3), "tb_s": round(tbs, 3), "frac_of_peak": round(tbs * 1e3 / HBM_PEAK_GBS, 4),
+            "workgroups": best[1], "bytes": nbytes,
+            "note": "a plain streaming read of the step's algorithmic bytes (decode_attn_read_probe), best of "
+                    "256-2048 workgroups, rotated buffers, back-to-back launches"}
+
+
+def oracle_single_thread(run_once, budget_s=3.0):
+    """Seconds per call of an oracle function on one host thread, over a few calls."""
+    n, t = 0, 0.0
+    while n < 1 or (t < budget_s and n < 100):
+        c0 = time.perf_counter()
+        run_once()
+        t += time.perf_counter() - c0
+        n += 1
+    return t / n, n
 
 
 def prefill_alg_bytes(wl):
@@ -218,7 +268,7 @@ def bench_gemm(args, wl):
             "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 5),
-            "traffic": None,
+            "traffic": traffic_from_profile(wl.name, "gemm_kernel"),
             "avg_launch_us": round(gpu_us, 3),
             "flops_per_launch": flops,
             "timing": "HIP events around the timed back-to-back launches on the bench stream",
@@ -249,26 +299,53 @@ def bench_gemm(args, wl):
             "kind": "oracle",
             "sample": "%d runs of the %dx%dx%d GEMM (fp64 C oracle, %d threads, %.1f s)" % (n, M, N, K, threads, t_cpu),
         }
+        sec, n1 = oracle_single_thread(lambda: oracle.gemm_f16(g["a"], g["b"], nthreads=1))
+        result["cpu_baseline"]["single_thread"] = {
+            "value": round(flops / sec / 1e12, 6), "us_per_step": round(sec * 1e6, 1), "cores": 1,
+            "sample": "%d runs of the GEMM on one thread" % n1}
     print(json.dumps(result), flush=True)
 
 
-def summarize_profile(args):
-    """profiles/<kernel>_<workload>.txt from a FETCH_SIZE run, a WRITE_SIZE run and a kernel-trace run."""
-    import csv
+KNOWN_KERNELS = ("decode_step_large_kernel", "decode_step_kernel", "attn_streamk_kernel", "gemm_kernel", "gemv_kernel",
+                 "prefill_kernel", "read_probe_kernel")
 
+
+def kernel_alg_bytes(args):
+    """{kernel name: algorithmic bytes per dispatch} for the kernels a run of --workload launches,
+    and the dominant kernel's name."""
     import decode_attention_output_amd as da
     import numpy as np
     import workloads
 
     wl = workloads.BY_NAME[args.workload]
     if isinstance(wl, workloads.PrefillWorkload):
-        kname, kbytes = "prefill_kernel", prefill_alg_bytes(wl)
-    else:
-        s = wl.shape
-        seq_lens = workloads.draw_seq_lens(wl, np.random.default_rng(wl.seed))
-        plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden,
-                                                 s.head_dim))
-        kname, kbytes, _ = dominant_kernel(wl, plan, seq_lens)
+        return {"prefill_kernel": prefill_alg_bytes(wl)}, "prefill_kernel"
+    if isinstance(wl, workloads.GemmWorkload):
+        return {"gemm_kernel": 2 * (wl.m * wl.k + wl.k * wl.n + wl.m * wl.n)}, "gemm_kernel"
+    s = wl.shape
+    seq_lens = workloads.draw_seq_lens(wl, np.random.default_rng(wl.seed))
+    tiles = json.loads(args.tiles) if args.tiles else None
+    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden,
+                                             s.head_dim, tiles=tiles))
+    kname, kbytes, _ = dominant_kernel(wl, plan, seq_lens)
+    D = s.head_dim
+    attn = 2 * 2 * s.num_kv_heads * D * int(np.sum(seq_lens)) + 2 * s.batch * s.num_q_heads * D + 2 * s.batch * s.o_in
+    proj = 2 * s.o_in * s.hidden + 2 * s.batch * s.o_in + 2 * s.batch * s.hidden
+    whole = workloads.algorithmic_bytes(s, seq_lens)
+    return {"decode_step_large_kernel": whole, "decode_step_kernel": whole, "attn_streamk_kernel": attn,
+            "gemm_kernel": proj, "gemv_kernel": proj, "read_probe_kernel": (whole + 15) // 16 * 16,
+            kname: kbytes}, kname
+
+
+def summarize_profile(args):
+    """profiles/<kernel>_<workload>[_<tag>].txt, for every kernel of the run, from a FETCH_SIZE run,
+    a WRITE_SIZE run and a kernel-trace run of the same bench command."""
+    import csv
+
+    import workloads
+
+    wl = workloads.BY_NAME[args.workload]
+    alg, dominant = kernel_alg_bytes(args)
 
     def counter_avg(path, counter, match):
         vals = []
@@ -278,53 +355,67 @@ def summarize_profile(args):
                     vals.append(float(row["Counter_Value"]))
         return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
-    is_dom = lambda n: kname in n
     is_cal = lambda n: "MulFunctor" in n
-    fetch_dom, nf = counter_avg(args.summarize_profile[0], "FETCH_SIZE", is_dom)
     fetch_cal, _ = counter_avg(args.summarize_profile[0], "FETCH_SIZE", is_cal)
-    write_dom, nw = counter_avg(args.summarize_profile[1], "WRITE_SIZE", is_dom)
     write_cal, _ = counter_avg(args.summarize_profile[1], "WRITE_SIZE", is_cal)
     f_scale = (CALIB_BYTES / 1024.0) / fetch_cal if fetch_cal else None
     w_scale = (CALIB_BYTES / 1024.0) / write_cal if write_cal else None
-    rd = fetch_dom * f_scale * 1024 if fetch_dom is not None and f_scale else None
-    wr = write_dom * w_scale * 1024 if write_dom is not None and w_scale else None
     stats = []
     with open(args.summarize_profile[2]) as f:
         for row in csv.DictReader(f):
             stats.append((row["Name"], int(row["Calls"]), float(row["AverageNs"]), float(row["MinNs"]),
                           float(row["MaxNs"])))
+    present = []
+    for name, *_ in stats:
+        k = next((k for k in KNOWN_KERNELS if re.search(r"\b%s\b" % k, re.sub(r"[^A-Za-z0-9_]", " ", name))), None)
+        if k and k not in present:
+            present.append(k)
+    extra = " --tiles '%s'" % args.tiles if args.tiles else ""
+    cmd_tail = "--workload %s --no-cpu-baseline --no-parity --no-graph%s" % (wl.name, extra)
     os.makedirs(PROFILES, exist_ok=True)
-    out = os.path.join(PROFILES, "%s_%s.txt" % (kname, wl.name))
-    with open(out, "w") as f:
-        f.write("# rocprofv3 summary: %s, workload %s\n" % (kname, wl.name))
-        f.write("# commands (run from the repository root on one MI355X):\n")
-        f.write("#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
-                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph\n" % wl.name)
-        f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- "
-                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph --steps 50\n" % wl.name)
-        f.write("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- "
-                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph --steps 50\n" % wl.name)
-        f.write("#   python3 bench.py --workload %s --summarize-profile <fetch csv> <write csv> <stats csv>\n"
-                % wl.name)
-        f.write("# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same counter reads\n")
-        f.write("# for a plain elementwise copy (torch mul by 1.0) of %d MiB read + %d MiB written.\n"
-                % (CALIB_BYTES >> 20, CALIB_BYTES >> 20))
-        f.write("# kernel trace (per kernel: calls, average / min / max ns):\n")
-        for name, calls, avg, mn, mx in stats:
-            f.write("#   %-90s %6d %12.1f %12.1f %12.1f\n" % (name[:90], calls, avg, mn, mx))
-        f.write("kernel = %s\n" % kname)
-        f.write("source_hash = %s\n" % kernel_source_hash())
-        f.write("algorithmic_bytes_per_dispatch = %d\n" % kbytes)
-        f.write("dispatches_counted = %d / %d\n" % (nf, nw))
-        f.write("fetch_kib_per_dispatch = %s\n" % fetch_dom)
-        f.write("write_kib_per_dispatch = %s\n" % write_dom)
-        f.write("fetch_scale = %s\nwrite_scale = %s\n" % (f_scale, w_scale))
-        f.write("hbm_read_bytes_per_dispatch = %s\n" % (None if rd is None else int(rd)))
-        f.write("hbm_write_bytes_per_dispatch = %s\n" % (None if wr is None else int(wr)))
-        f.write("hbm_bytes_per_dispatch = %s\n" % (None if rd is None or wr is None else int(rd + wr)))
-        dom_avg = [avg for name, _, avg, _, _ in stats if kname in name]
-        f.write("trace_avg_ns = %s\n" % (dom_avg[0] if dom_avg else None))
-    print(out)
+    tag = ("_" + args.profile_tag) if args.profile_tag else ""
+    for kname in present:
+        match = lambda n, k=kname: re.search(r"\b%s\b" % k, re.sub(r"[^A-Za-z0-9_]", " ", n)) is not None
+        fetch, nf = counter_avg(args.summarize_profile[0], "FETCH_SIZE", match)
+        write, nw = counter_avg(args.summarize_profile[1], "WRITE_SIZE", match)
+        rd = fetch * f_scale * 1024 if fetch is not None and f_scale else None
+        wr = write * w_scale * 1024 if write is not None and w_scale else None
+        kbytes = alg.get(kname)
+        out = os.path.join(PROFILES, "%s_%s%s.txt" % (kname, wl.name, tag))
+        with open(out, "w") as f:
+            f.write("# rocprofv3 summary: %s, workload %s%s\n" % (kname, wl.name,
+                                                                  (" (" + args.profile_tag + ")") if tag else ""))
+            f.write("# commands (run from the repository root on one MI355X):\n")
+            f.write("#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python3 bench.py %s\n"
+                    % cmd_tail)
+            f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- python3 bench.py %s "
+                    "--steps 50\n" % cmd_tail)
+            f.write("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- python3 bench.py %s "
+                    "--steps 50\n" % cmd_tail)
+            f.write("#   python3 bench.py %s --summarize-profile <fetch csv> <write csv> <stats csv>%s\n"
+                    % (cmd_tail, (" --profile-tag " + args.profile_tag) if tag else ""))
+            f.write("# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same counter reads\n")
+            f.write("# for a plain elementwise copy (torch mul by 1.0) of %d MiB read + %d MiB written.\n"
+                    % (CALIB_BYTES >> 20, CALIB_BYTES >> 20))
+            f.write("# kernel trace (per kernel: calls, average / min / max ns):\n")
+            for name, calls, avg, mn, mx in stats:
+                f.write("#   %-90s %6d %12.1f %12.1f %12.1f\n" % (name[:90], calls, avg, mn, mx))
+            f.write("kernel = %s\n" % kname)
+            f.write("dominant = %s\n" % (kname == dominant))
+            f.write("source_hash = %s\n" % kernel_source_hash())
+            f.write("algorithmic_bytes_per_dispatch = %s\n" % kbytes)
+            f.write("dispatches_counted = %d / %d\n" % (nf, nw))
+            f.write("fetch_kib_per_dispatch = %s\n" % fetch)
+            f.write("write_kib_per_dispatch = %s\n" % write)
+            f.write("fetch_scale = %s\nwrite_scale = %s\n" % (f_scale, w_scale))
+            f.write("hbm_read_bytes_per_dispatch = %s\n" % (None if rd is None else int(rd)))
+            f.write("hbm_write_bytes_per_dispatch = %s\n" % (None if wr is None else int(wr)))
+            f.write("hbm_bytes_per_dispatch = %s\n" % (None if rd is None or wr is None else int(rd + wr)))
+            dom_avg = [avg for name, _, avg, _, _ in stats if match(name)]
+            f.write("trace_avg_ns = %s\n" % (dom_avg[0] if dom_avg else None))
+            if dom_avg and kbytes:
+                f.write("achieved_gb_s = %.1f\n" % (kbytes / dom_avg[0]))
+        print(out)
 
 
 def summarize_mfma(args):
@@ -403,8 +494,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--tiles", default=None,
+                    help="JSON tile override of the decode step (decode_attn_tiles_t fields), e.g. "
+                         "'{\"step_mode\": 2, \"proj_tile_n\": 256}'")
+    ap.add_argument("--no-floor", action="store_true", help="skip the streaming-read floor of the step's bytes")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "TRACE_STATS_CSV"),
                     help="write the PMC/trace summary of a profiled run to profiles/ and exit")
+    ap.add_argument("--profile-tag", default="", help="suffix of the summary file names (a tile variant)")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("KERNEL", "PMC_CSV", "TRACE_STATS_CSV"),
                     help="write the matrix-core counter summary of kernel KERNEL (a name prefix) in a profiled run "
                          "of --workload to profiles/ and exit")
@@ -469,11 +565,13 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.set_stream(stream)
 
+    tiles = json.loads(args.tiles) if args.tiles else None
     for st in sets:
         st["step"] = da.DecodeStep(st["q"], st["k"], st["v"], sl, st["o_weight"], out=st["out"], workspace=st["ws"],
-                                   stream=stream)
+                                   stream=stream, tiles=tiles)
 
-    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden, s.head_dim))
+    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden, s.head_dim,
+                                             tiles=tiles))
 
     # ---- warm-up, then exactly `steps` timed steps (one prepared C-ABI call each) ----
     for i in range(args.warmup):
@@ -524,7 +622,8 @@ def main():
     # kernel's launch duration (the rocprofv3 kernel trace of the same command agrees).
     n_b = args.breakdown_steps
     for st in sets:
-        st["attn"] = da.AttentionStep(st["q"], st["k"], st["v"], sl, out=st["flat"], workspace=st["ws"], stream=stream)
+        st["attn"] = da.AttentionStep(st["q"], st["k"], st["v"], sl, out=st["flat"], workspace=st["ws"], stream=stream,
+                                      tiles=tiles)
         st["proj"] = da.OprojStep(st["flat"], st["o_weight"], out=st["out"], workspace=st["ws"], stream=stream)
 
     def avg_launch_us(name):
@@ -544,6 +643,11 @@ def main():
     # restore the step's own output in set 0 for the parity check
     sets[0]["step"]()
     torch.cuda.synchronize()
+    # the single-launch steps' bounded waits never gave up in any of the calls above
+    step_status = [da.decode_attn_step_status(st["ws"], stream) for st in sets]
+    if any(rc != da.DA_OK for rc in step_status):
+        raise da.DecodeAttnError(next(rc for rc in step_status if rc != da.DA_OK), "decode step (status)")
+    floor = None if args.no_floor else stream_floor(alg_bytes, stream, args.min_rotate_mib)
 
     kname, kbytes, which = dominant_kernel(wl, plan, seq_lens)
     dom_us = {"oproj": oproj_us, "attention": attn_us, "step": step_us}[which]
@@ -603,7 +707,11 @@ def main():
         },
         "breakdown_us": {"step": round(step_us, 3), "attention_alone": round(attn_us, 3),
                          "oproj_alone": round(oproj_us, 3)},
+        "stream_floor": floor,
+        "step_status": "ok",
     }
+    if tiles:
+        result["config"]["tiles"] = tiles
 
     if not args.no_parity or not args.no_cpu_baseline:
         import oracle
@@ -634,6 +742,13 @@ def main():
             "kind": "oracle",
             "sample": "%d full decode steps of %s (fp64 C oracle, %d threads, %.1f s)" % (n, wl.name, threads, t_cpu),
         }
+        if wl.name in (workloads.TINY.name, workloads.PAGES.name):
+            # the same oracle on one host thread
+            sec, n1 = oracle_single_thread(lambda: oracle.decode_step(full["q"], full["k"], full["v"], full["seq_lens"],
+                                                                      full["o_weight"], nthreads=1))
+            result["cpu_baseline"]["single_thread"] = {
+                "value": round(alg_bytes / sec / 1e12, 6), "us_per_step": round(sec * 1e6, 1), "cores": 1,
+                "sample": "%d full decode steps on one thread" % n1}
     print(json.dumps(result), flush=True)
 
 

@@ -9,7 +9,8 @@ raises.
 The names mirror the C entry points: ``decode_attn_fwd``, ``decode_attn_only``,
 ``oproj_fwd``, ``gemm_f16``, ``decode_attn_workspace_size``,
 ``oproj_workspace_size``, ``decode_attn_plan``, ``decode_attn_status_str``,
-``prefill_attn_fwd``, ``decode_attn_step_status``, ``decode_attn_fwd_noalloc``.
+``prefill_attn_fwd``, ``decode_attn_step_status``, ``decode_attn_fwd_noalloc``,
+``decode_attn_read_probe`` (a plain streaming read, the measurement floor).
 
 Before any call reaches the library, the torch wrappers check that the
 tensors agree with each other (batch, heads, head_dim, cache length,
@@ -50,6 +51,7 @@ EXPORTED = (
     "prefill_attn_fwd",
     "decode_attn_step_status",
     "decode_attn_fwd_noalloc",
+    "decode_attn_read_probe",
 )
 
 
@@ -152,6 +154,8 @@ def load_library(path: str = LIB_PATH):
     lib.prefill_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(PrefillAttnShape), vp]
     lib.decode_attn_fwd_noalloc.restype = ctypes.c_int
     lib.decode_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, shp, vp]
+    lib.decode_attn_read_probe.restype = ctypes.c_int
+    lib.decode_attn_read_probe.argtypes = [vp, sz, vp, i32, vp]
     lib.decode_attn_step_status.restype = ctypes.c_int
     lib.decode_attn_step_status.argtypes = [vp, sz, vp]
     lib.decode_attn_status_str.restype = ctypes.c_char_p

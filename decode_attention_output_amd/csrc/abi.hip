@@ -773,6 +773,14 @@ int prefill_attn_fwd(const void* q, const void* k_cache, const void* v_cache, co
   return da::launch_prefill(p, (hipStream_t)stream) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
+int decode_attn_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+  if (!src || !sink) return DA_ERR_NULL;
+  if (misaligned(src, 16) || misaligned(sink, 4)) return DA_ERR_ALIGN;
+  if (bytes == 0 || bytes % 16 != 0 || workgroups < 1 || workgroups > 65536) return DA_ERR_SHAPE;
+  return da::launch_read_probe(src, bytes, sink, workgroups, (hipStream_t)stream) == hipSuccess ? DA_OK
+                                                                                               : DA_ERR_LAUNCH;
+}
+
 int decode_attn_step_status(const void* workspace, size_t workspace_bytes, void* stream) {
   const bool own = workspace == nullptr;  // the no-allocation scratch of the current device
   if (!own) {

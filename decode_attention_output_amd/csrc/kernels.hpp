@@ -168,6 +168,9 @@ struct PrefillParams {
 };
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t s);
 
+// A plain streaming read of `bytes` (a multiple of 16) by `workgroups` workgroups; one word per workgroup to sink.
+hipError_t launch_read_probe(const void* src, uint64_t bytes, uint32_t* sink, int workgroups, hipStream_t s);
+
 hipError_t launch_gemv(const GemvParams& p, int mpad, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_f16(const GemmParams& p, hipStream_t s);

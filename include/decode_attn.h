@@ -316,6 +316,18 @@ int prefill_attn_fwd(const void* q_dev, const void* k_cache_dev, const void* v_c
                      const int32_t* ctx_lens_dev, void* out_dev, const prefill_attn_shape_t* shape,
                      void* stream);
 
+/*
+ * Measurement aid, not part of the step: a plain streaming read of `bytes`
+ * (a multiple of 16) from src_dev by `workgroups` 256-thread workgroups, each
+ * reading its contiguous share in 1 KiB blocks (the attention's K/V load
+ * pattern); sink_dev receives one uint32 per workgroup. Timing it on a decode
+ * step's algorithmic bytes gives the floor a step of that size is compared
+ * with, as the profiler-backed verification of the MT-S page (section 5,
+ * 性能验证) asks. Returns DA_ERR_NULL / DA_ERR_ALIGN / DA_ERR_SHAPE before any
+ * HIP call, DA_ERR_LAUNCH if the launch fails; work is enqueued on `stream`.
+ */
+int decode_attn_read_probe(const void* src_dev, size_t bytes, uint32_t* sink_dev, int32_t workgroups, void* stream);
+
 /* Static text for a status code. */
 const char* decode_attn_status_str(int status);
 

@@ -134,6 +134,15 @@ def test_noalloc_entry_checks_arguments_before_any_hip_call(lib):
     assert call(big) == da.DA_ERR_WORKSPACE
 
 
+def test_read_probe_argument_checks(lib):
+    sink = FAKE + 256
+    assert lib.decode_attn_read_probe(None, 1024, sink, 8, None) == da.DA_ERR_NULL
+    assert lib.decode_attn_read_probe(FAKE, 1024, None, 8, None) == da.DA_ERR_NULL
+    assert lib.decode_attn_read_probe(FAKE + 8, 1024, sink, 8, None) == da.DA_ERR_ALIGN
+    assert lib.decode_attn_read_probe(FAKE, 1000, sink, 8, None) == da.DA_ERR_SHAPE
+    assert lib.decode_attn_read_probe(FAKE, 1024, sink, 0, None) == da.DA_ERR_SHAPE
+
+
 def test_step_wait_polls_in_range_is_accepted(lib):
     for polls in (1, 1000, 1 << 24):
         assert da.decode_attn_workspace_size(_shape(tiles=dict(step_wait_polls=polls))) > 0

@@ -506,3 +506,21 @@ def test_single_launch_large_step_timeout_is_reported(gpu):
     _status_ok(ws, "after the counters were zero-filled")
     _counter_block_is_clear(ws)
     _check_step(inp, {"flat": flat, "out": out}, what="large step after a timeout")
+
+
+def test_read_probe_reads_every_byte(gpu):
+    # the measurement probe folds its share of the words with xor: every 16-byte unit is read once
+    rng = np.random.default_rng(81)
+    n16, W = 5000, 7
+    words = rng.integers(0, 2 ** 32, size=(n16, 4), dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros(W, dtype=torch.int32, device="cuda")
+    rc = da.load_library().decode_attn_read_probe(src.data_ptr(), n16 * 16, sink.data_ptr(), W,
+                                                  torch.cuda.current_stream().cuda_stream)
+    assert rc == da.DA_OK
+    got = sink.cpu().numpy().view(np.uint32)
+    for w in range(W):
+        b0 = (n16 * w // W) & ~63
+        b1 = n16 if w + 1 == W else (n16 * (w + 1) // W) & ~63
+        want = np.bitwise_xor.reduce(words[b0:b1].ravel()) if b1 > b0 else np.uint32(0)
+        assert got[w] == want, w

@@ -87,3 +87,46 @@ def test_mfma_summary_from_counter_and_trace_csvs(tmp_path, monkeypatch):
     assert float(fields["mfma_busy_pct_at_peak_clock"]) == round(100.0 * 102400 / (5000.0 * 2.4 * 1024), 3)
     assert float(fields["trace_avg_ns"]) == 5000.0
     assert float(fields["executed_mfma_tflops"]) == round(524288 * 512 / 5000.0 / 1e3, 2)
+
+
+def test_traffic_summaries_for_every_kernel_of_the_run(tmp_path, monkeypatch):
+    # FETCH / WRITE KiB per dispatch of each kernel, scaled by what the counters read for the 64 MiB
+    # calibration copy (here 2x too much read, exact write), one summary file per kernel
+    import bench
+    import workloads
+
+    def pmc(path, counter, vals):
+        rows = ["Kernel_Name,Counter_Name,Counter_Value"]
+        rows += ["%s,%s,%s" % (k, counter, v) for k, v in vals]
+        path.write_text("\n".join(rows) + "\n")
+
+    attn = "void da::(anonymous namespace)::attn_streamk_kernel<4; 4; 1; 128>(da::AttnParams)"
+    gemm = "void da::(anonymous namespace)::gemm_kernel<false; 1; 2>(da::GemmParams)"
+    cal = "void at::native::elementwise_kernel<MulFunctor>"
+    fetch, write, stats = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "s.csv"
+    pmc(fetch, "FETCH_SIZE", [(attn, 1000.0), (attn, 3000.0), (gemm, 500.0), (cal, 2 * 65536.0)])
+    pmc(write, "WRITE_SIZE", [(attn, 10.0), (attn, 30.0), (gemm, 5.0), (cal, 65536.0)])
+    stats.write_text("Name,Calls,AverageNs,MinNs,MaxNs\n%s,5,50000.0,1.0,2.0\n%s,5,12000.0,1.0,2.0\n%s,1,9.0,9.0,9.0\n"
+                     % (attn, gemm, cal))
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+
+    class A:
+        workload = workloads.BATCHED.name
+        tiles = '{"step_mode": 2}'
+        profile_tag = "two_launches"
+        summarize_profile = (str(fetch), str(write), str(stats))
+
+    bench.summarize_profile(A())
+    files = sorted(p.name for p in (tmp_path / "profiles").iterdir())
+    assert files == ["attn_streamk_kernel_%s_two_launches.txt" % workloads.BATCHED.name,
+                     "gemm_kernel_%s_two_launches.txt" % workloads.BATCHED.name]
+    text = (tmp_path / "profiles" / files[0]).read_text()
+    fields = dict(l.split(" = ", 1) for l in text.splitlines() if " = " in l and not l.startswith("#"))
+    assert fields["kernel"] == "attn_streamk_kernel" and fields["dominant"] == "True"
+    assert int(fields["hbm_read_bytes_per_dispatch"]) == 2000 * 512   # 2000 KiB at half scale
+    assert int(fields["hbm_write_bytes_per_dispatch"]) == 20 * 1024
+    assert float(fields["trace_avg_ns"]) == 50000.0
+    assert "--tiles '{\"step_mode\": 2}'" in text
+    gfields = dict(l.split(" = ", 1) for l in (tmp_path / "profiles" / files[1]).read_text().splitlines()
+                   if " = " in l and not l.startswith("#"))
+    assert gfields["dominant"] == "False" and int(gfields["hbm_read_bytes_per_dispatch"]) == 500 * 512
