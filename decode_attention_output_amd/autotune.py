@@ -1,28 +1,34 @@
-"""Measured tile search for one decode-step shape.
+"""Measured tile search: per-shape table rows and built-in rules.
 
 The per-matmul tile lesson of "PyPTO 开箱性能调优实战：Decode Attention 多 Matmul
 独立 TileShape 配置 F-16" (sections 核心原则 and 迭代过程) is that each matmul of
-the step needs its own tile and that the right one is found by measuring. This
-tool does that search on the GPU through the C ABI's tile override
-(decode_attn_tiles_t), one matmul group at a time:
+the step needs its own tile and that the right one is found by measuring; the
+page "CCCL → Triton 方法论迁移" (section 一) adds how a rule is chosen: run every
+candidate on several problem sizes and keep the one with the best geometric
+mean. This tool does both on the GPU through the C ABI's tile override
+(decode_attn_tiles_t):
 
-  1. attention (QK^T, softmax, attn x V): stream-K workgroups x pipeline depth,
-     timed with decode_attn_only;
-  2. projection (attn_output_flat x o_weight): column tile x K split, timed as
-     the whole step in two launches with the best attention tiles;
-  3. where the single-launch step supports the shape: its attention pieces x
-     projection column tile, against two launches.
+  search   one shape: attention tiles (stream-K workgroups x pipeline depth x
+           the per-sequence charge), then projection tiles (column tile x K
+           split) with two launches, then the single-launch step's own knobs,
+           against the built-in choice. With --emit the winner becomes the
+           shape's row of the measured tile table (csrc/tile_table.inc) only if
+           it beats the built-in choice by more than the repeat spread of the
+           two (otherwise the row is removed: the built-in rules serve it).
+  rules    candidate settings applied to every shape of a set (by default the
+           benchmarked decode workloads and the one-GPU shares of a sharded
+           step); each candidate's time is divided by the built-in time of the
+           same shape, and the candidate with the best geometric mean of those
+           ratios is reported as the rule to build in.
 
 Every candidate is timed over rotated copies of the inputs (at least 512 MiB,
-twice the Infinity Cache) with HIP events on one stream, median of several
-repeats, and its output is compared with the built-in choice's output (two
-correct results differ by at most a couple of bf16 ulps). The result is one
-JSON line per candidate and a final line with the best tiles; with --emit the
-best tiles become the shape's row of the measured tile table
-(csrc/tile_table.inc), which the library consults for calls without an
-override of their own (rebuild after emitting).
+twice the Infinity Cache) with HIP events on one stream; a measurement is the
+median of several repeats, its spread the difference between the slowest and
+the fastest repeat. Every candidate's output is compared with the built-in
+choice's (two correct results differ by at most a couple of bf16 ulps).
 
-    python -m decode_attention_output_amd.autotune --workload decode_b4_h64kv8_L32768_o8192 --emit
+    python -m decode_attention_output_amd.autotune search --workload decode_b4_h64kv8_L32768_o8192 --emit
+    python -m decode_attention_output_amd.autotune rules
 """
 from __future__ import annotations
 
@@ -36,38 +42,65 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+TABLE = os.path.join(HERE, "csrc", "tile_table.inc")
+TILE_FIELDS = ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit", "step_mode", "attn_seq_cost",
+               "step_weight_delay")
 
 
 def _parse_list(text):
     return [int(x) for x in text.split(",") if x.strip()]
 
 
-def parse(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--workload", required=True)
-    ap.add_argument("--attn-wgs", default="128,192,256,320,384,512,768")
-    ap.add_argument("--attn-depth", default="1,2,3")
-    ap.add_argument("--tile-n", default="64,128,256,512")
-    ap.add_argument("--ksplit", default="0,1,2,4,8,16,32")
-    ap.add_argument("--launches", type=int, default=100, help="timed launches per repeat")
-    ap.add_argument("--repeats", type=int, default=5)
-    ap.add_argument("--min-rotate-mib", type=float, default=512.0)
-    ap.add_argument("--step-wgs", default="32,64,96,128,192,256",
-                    help="attention workgroups aimed at in the single-launch step")
-    ap.add_argument("--skip", default="", help="comma list of stages to skip: attn,proj,mode")
-    ap.add_argument("--emit", action="store_true", help="write the best tiles into csrc/tile_table.inc")
-    ap.add_argument("--table", default=TABLE, help=argparse.SUPPRESS)
-    return ap.parse_args(argv)
+# ---- selection logic (host only) ------------------------------------------
+
+class Timing:
+    """Repeat times of one measurement (µs per launch)."""
+
+    def __init__(self, samples):
+        self.samples = list(samples)
+
+    @property
+    def median(self):
+        return statistics.median(self.samples)
+
+    @property
+    def spread(self):
+        return max(self.samples) - min(self.samples)
+
+    def as_dict(self):
+        return {"median_us": round(self.median, 3), "spread_us": round(self.spread, 3),
+                "samples": [round(x, 3) for x in self.samples]}
 
 
-TABLE = os.path.join(HERE, "csrc", "tile_table.inc")
-TILE_FIELDS = ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit", "step_mode")
+def significant(best: Timing, builtin: Timing) -> bool:
+    """A candidate replaces the built-in choice only if its median is lower by more than
+    the larger of the two repeat spreads (a smaller gap is inside the measurement noise)."""
+    return builtin.median - best.median > max(best.spread, builtin.spread)
+
+
+def geomean(values):
+    values = list(values)
+    return math.exp(sum(math.log(v) for v in values) / len(values))
+
+
+def select_rule(times):
+    """times: {candidate key: {shape: Timing}} with the built-in choice under key None.
+    Returns (best key, {key: geometric mean of candidate / built-in medians}); a candidate
+    must have run on every shape the built-in ran on (missing = not allowed there)."""
+    base = times[None]
+    ratios = {}
+    for key, per_shape in times.items():
+        if set(per_shape) != set(base):
+            continue
+        ratios[key] = geomean(per_shape[s].median / base[s].median for s in base)
+    best = min(ratios, key=lambda k: (ratios[k], k is not None))
+    return best, ratios
 
 
 def emit_entry(path, shape, tiles, note):
     """Insert or replace the table row of `shape` (a dict of batch, num_q_heads, num_kv_heads,
     head_dim, max_seq_len, hidden); the header comment and the other rows are kept, rows sorted
-    by shape."""
+    by shape. `tiles` None removes the shape's row."""
     key = (shape["batch"], shape["num_q_heads"], shape["num_kv_heads"], shape["head_dim"], shape["max_seq_len"],
            shape["hidden"])
     head, rows = [], {}
@@ -78,145 +111,242 @@ def emit_entry(path, shape, tiles, note):
                 rows[tuple(vals[:6])] = line
             else:
                 head.append(line)
-    vals = list(key) + [int(tiles.get(n, 0)) for n in TILE_FIELDS]
-    rows[key] = "TILE_ENTRY(%s)  // %s\n" % (", ".join(str(v) for v in vals), note)
+    if tiles is None:
+        rows.pop(key, None)
+    else:
+        vals = list(key) + [int(tiles.get(n, 0)) for n in TILE_FIELDS]
+        rows[key] = "TILE_ENTRY(%s)  // %s\n" % (", ".join(str(v) for v in vals), note)
     with open(path, "w") as f:
         f.writelines(head)
         f.writelines(rows[k] for k in sorted(rows))
+
+
+# ---- measurement on the GPU ------------------------------------------------
+
+class Bench:
+    """Seeded inputs of one decode workload in rotated copies, and timers of prepared calls."""
+
+    def __init__(self, wl, launches, repeats, min_rotate_mib):
+        import numpy as np
+        import torch
+
+        import decode_attention_output_amd as da
+        import workloads
+
+        self.da, self.np, self.torch, self.wl = da, np, torch, wl
+        self.launches, self.repeats = launches, repeats
+        s = wl.shape
+        dev = torch.device("cuda:0")
+        inp = workloads.decode_inputs(wl, poison=True)
+        self.seq_lens = inp["seq_lens"]
+        self.alg_bytes = workloads.algorithmic_bytes(s, self.seq_lens)
+        self.kv_bytes = 2 * 2 * s.num_kv_heads * s.head_dim * int(np.sum(self.seq_lens))
+
+        def to_dev(words):
+            return torch.from_numpy(np.ascontiguousarray(words).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        base = {n: to_dev(inp[n]) for n in ("q", "k", "v", "o_weight")}
+        del inp
+        self.sl = torch.from_numpy(self.seq_lens).to(dev)
+        R = max(1, math.ceil(min_rotate_mib * 2 ** 20 / self.alg_bytes))
+        self.sets = []
+        for r in range(R):
+            st = {n: (t if r == 0 else t.clone()) for n, t in base.items()}
+            st["out"] = torch.empty((s.batch, s.hidden), dtype=torch.bfloat16, device=dev)
+            st["flat"] = torch.empty((s.batch, s.o_in), dtype=torch.bfloat16, device=dev)
+            st["ws"] = da.Workspace(dev)
+            self.sets.append(st)
+        self.stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        self.ref = {}
+        self.ref["flat"] = self._run_ref(self.attn_calls(None), "flat")
+        self.ref["out"] = self._run_ref(self.step_calls(None), "out")
+
+    def _run_ref(self, calls, which):
+        calls[0]()
+        self.torch.cuda.synchronize()
+        return self.bf16_to_f64(self.sets[0][which])
+
+    def bf16_to_f64(self, t):
+        torch, np = self.torch, self.np
+        return torch.from_numpy(t.cpu().view(torch.int16).numpy()).view(torch.bfloat16).double().numpy()
+
+    def attn_calls(self, tiles):
+        da = self.da
+        return [da.AttentionStep(st["q"], st["k"], st["v"], self.sl, out=st["flat"], workspace=st["ws"],
+                                 stream=self.stream, tiles=tiles) for st in self.sets]
+
+    def step_calls(self, tiles):
+        da = self.da
+        return [da.DecodeStep(st["q"], st["k"], st["v"], self.sl, st["o_weight"], out=st["out"], workspace=st["ws"],
+                              stream=self.stream, tiles=tiles) for st in self.sets]
+
+    def time(self, calls):
+        torch = self.torch
+        for i in range(max(20, len(calls))):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        res = []
+        for _ in range(self.repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            for i in range(self.launches):
+                calls[i % len(calls)]()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e3 / self.launches)
+        return Timing(res)
+
+    def try_tiles(self, tiles, which="out"):
+        """Timing of the step (which="out") or of the attention alone (which="flat") under `tiles`,
+        or None if the tiles are outside what the shape allows or change the result."""
+        np = self.np
+        try:
+            calls = self.step_calls(tiles) if which == "out" else self.attn_calls(tiles)
+        except self.da.DecodeAttnError:
+            return None
+        t = self.time(calls)
+        calls[0]()
+        self.torch.cuda.synchronize()
+        got, ref = self.bf16_to_f64(self.sets[0][which]), self.ref[which]
+        err = np.abs(got - ref)
+        if not np.all(np.isfinite(got)) or (err > 2.0 ** -6 * np.maximum(np.abs(ref), 1e-2)).any():
+            return None
+        if any(self.da.decode_attn_step_status(st["ws"], self.stream) != self.da.DA_OK for st in self.sets):
+            return None
+        return t
+
+    def shape(self):
+        s = self.wl.shape
+        return {"batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+                "max_seq_len": s.max_seq_len, "hidden": s.hidden, "head_dim": s.head_dim}
+
+
+def parse(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    sub = ap.add_subparsers(dest="mode", required=True)
+    for name in ("search", "rules"):
+        p = sub.add_parser(name)
+        p.add_argument("--launches", type=int, default=100, help="timed launches per repeat")
+        p.add_argument("--repeats", type=int, default=7)
+        p.add_argument("--min-rotate-mib", type=float, default=512.0)
+    s = sub.choices["search"]
+    s.add_argument("--workload", required=True)
+    s.add_argument("--attn-wgs", default="128,160,192,224,256,384")
+    s.add_argument("--attn-depth", default="1,2")
+    s.add_argument("--seq-cost", default="1,3,6,12")
+    s.add_argument("--tile-n", default="64,128,256,512")
+    s.add_argument("--ksplit", default="0,2,4,8,16")
+    s.add_argument("--step-wgs", default="64,96,128,192,256",
+                   help="attention workgroups aimed at in the single-launch step")
+    s.add_argument("--weight-delay", default="0,50,100", help="single-launch step: weight delay, 10 ns ticks")
+    s.add_argument("--skip", default="", help="comma list of stages to skip: attn,proj,mode")
+    s.add_argument("--emit", action="store_true", help="write (or remove) the shape's row of csrc/tile_table.inc")
+    s.add_argument("--table", default=TABLE, help=argparse.SUPPRESS)
+    r = sub.choices["rules"]
+    r.add_argument("--shapes", default="", help="comma list of workload names (default: the benchmarked decode "
+                                                 "workloads and the one-GPU shares of sharded steps)")
+    r.add_argument("--candidates", default="", help="JSON list of tile dicts applied to every shape")
+    return ap.parse_args(argv)
+
+
+DEFAULT_RULE_CANDIDATES = [
+    {"attn_workgroups": 160}, {"attn_workgroups": 224}, {"attn_workgroups": 256},
+    {"attn_seq_cost": 1}, {"attn_seq_cost": 3}, {"attn_seq_cost": 12},
+    {"proj_ksplit": 2}, {"proj_ksplit": 8},
+]
+
+
+def run_search(args):
+    import workloads
+
+    wl = workloads.BY_NAME[args.workload]
+    b = Bench(wl, args.launches, args.repeats, args.min_rotate_mib)
+    da = b.da
+    skip = set(x for x in args.skip.split(",") if x)
+
+    def report(stage, tiles, t):
+        row = {"stage": stage, "tiles": tiles, "ok": t is not None}
+        if t is not None:
+            row.update(t.as_dict())
+        print(json.dumps(row), flush=True)
+        return t
+
+    builtin = report("builtin", {}, b.try_tiles({}))
+    best, best_t = {}, builtin
+    plan = da.decode_attn_plan(da.make_shape(**b.shape()))
+    if "attn" not in skip and plan.fused != 1:
+        base_attn = report("attn", {}, b.try_tiles({}, "flat"))
+        best_a, best_at = {}, base_attn
+        for w, d, c in itertools.product(_parse_list(args.attn_wgs), _parse_list(args.attn_depth),
+                                         _parse_list(args.seq_cost)):
+            t = {"attn_workgroups": w, "attn_depth": d, "attn_seq_cost": c}
+            tm = report("attn", t, b.try_tiles(t, "flat"))
+            if tm is not None and tm.median < best_at.median:
+                best_a, best_at = t, tm
+        for tn, ks in itertools.product(_parse_list(args.tile_n), _parse_list(args.ksplit)):
+            t = dict(best_a, proj_tile_n=tn, proj_ksplit=ks)
+            tm = report("proj", t, b.try_tiles(t))
+            if tm is not None and tm.median < best_t.median:
+                best, best_t = t, tm
+    if "mode" not in skip and plan.fused == 1:
+        for w, tn, dl in itertools.product([0] + _parse_list(args.step_wgs), [0, 128, 256, 512],
+                                           _parse_list(args.weight_delay)):
+            t = {"step_mode": 1, "attn_workgroups": w, "proj_tile_n": tn, "step_weight_delay": dl}
+            tm = report("mode", t, b.try_tiles(t))
+            if tm is not None and tm.median < best_t.median:
+                best, best_t = t, tm
+    # the winner again, beside the built-in choice, so that both spreads come from the same moment
+    final_best = b.try_tiles(best) if best else builtin
+    final_builtin = b.try_tiles({})
+    keep = bool(best) and final_best is not None and significant(final_best, final_builtin)
+    summary = {"workload": wl.name, "best": best, "best_timing": final_best.as_dict(),
+               "builtin_timing": final_builtin.as_dict(), "significant": keep, "shape": b.shape()}
+    print(json.dumps(summary), flush=True)
+    if args.emit:
+        emit_entry(args.table, b.shape(), best if keep else None, "%s: %.2f us (built-in %.2f us, spread %.2f)" % (
+            wl.name, final_best.median, final_builtin.median, max(final_best.spread, final_builtin.spread)))
+
+
+def run_rules(args):
+    import workloads
+
+    names = [x for x in args.shapes.split(",") if x] or [w.name for w in workloads.RULE_SHAPES]
+    cands = json.loads(args.candidates) if args.candidates else DEFAULT_RULE_CANDIDATES
+    times = {None: {}}
+    for name in names:
+        b = Bench(workloads.BY_NAME[name], args.launches, args.repeats, args.min_rotate_mib)
+        t0 = b.try_tiles({})
+        times[None][name] = t0
+        print(json.dumps({"shape": name, "tiles": {}, **t0.as_dict()}), flush=True)
+        for c in cands:
+            t = b.try_tiles(c)
+            key = json.dumps(c, sort_keys=True)
+            if t is not None:
+                times.setdefault(key, {})[name] = t
+            print(json.dumps({"shape": name, "tiles": c, "ok": t is not None,
+                              **(t.as_dict() if t is not None else {})}), flush=True)
+        del b
+    best, ratios = select_rule(times)
+    print(json.dumps({"geomean_ratio_vs_builtin": {("builtin" if k is None else k): round(v, 4)
+                                                   for k, v in sorted(ratios.items(), key=lambda kv: kv[1])},
+                      "best": None if best is None else json.loads(best)}), flush=True)
 
 
 def main(argv=None):
     args = parse(argv)
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
-    import numpy as np
     import torch
 
     import decode_attention_output_amd as da
-    import workloads
 
-    wl = workloads.BY_NAME[args.workload]
-    s = wl.shape
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    torch.cuda.set_device(0)
     da.load_library()
-    inp = workloads.decode_inputs(wl, poison=True)
-    seq_lens = inp["seq_lens"]
-    alg_bytes = workloads.algorithmic_bytes(s, seq_lens)
-
-    def to_dev(words):
-        return torch.from_numpy(np.ascontiguousarray(words).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    base = {n: to_dev(inp[n]) for n in ("q", "k", "v", "o_weight")}
-    del inp
-    sl = torch.from_numpy(seq_lens).to(dev)
-    R = max(1, math.ceil(args.min_rotate_mib * 2 ** 20 / alg_bytes))
-    sets = []
-    for r in range(R):
-        st = {n: (t if r == 0 else t.clone()) for n, t in base.items()}
-        st["out"] = torch.empty((s.batch, s.hidden), dtype=torch.bfloat16, device=dev)
-        st["flat"] = torch.empty((s.batch, s.o_in), dtype=torch.bfloat16, device=dev)
-        st["ws"] = da.Workspace(dev)
-        sets.append(st)
-    stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    torch.cuda.set_stream(stream)
-
-    def time_calls(calls):
-        """Median µs per launch of the prepared calls, cycled over the rotation sets."""
-        for i in range(max(10, len(calls))):
-            calls[i % len(calls)]()
-        torch.cuda.synchronize()
-        res = []
-        for _ in range(args.repeats):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(args.launches):
-                calls[i % len(calls)]()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            res.append(e0.elapsed_time(e1) * 1e3 / args.launches)
-        return statistics.median(res)
-
-    def bf16_to_f64(t):
-        return torch.from_numpy(t.cpu().view(torch.int16).numpy()).view(torch.bfloat16).double().numpy()
-
-    def differs(got, ref):
-        err = np.abs(got - ref)
-        return bool(not np.all(np.isfinite(got)) or (err > 2.0 ** -6 * np.maximum(np.abs(ref), 1e-2)).any())
-
-    def attn_calls(tiles):
-        return [da.AttentionStep(st["q"], st["k"], st["v"], sl, out=st["flat"], workspace=st["ws"], stream=stream,
-                                 tiles=tiles) for st in sets]
-
-    def step_calls(tiles):
-        return [da.DecodeStep(st["q"], st["k"], st["v"], sl, st["o_weight"], out=st["out"], workspace=st["ws"],
-                              stream=stream, tiles=tiles) for st in sets]
-
-    # outputs of the built-in choice: the reference every candidate must agree with
-    attn_calls(None)[0]()
-    step_calls(None)[0]()
-    torch.cuda.synchronize()
-    ref_flat = bf16_to_f64(sets[0]["flat"])
-    ref_out = bf16_to_f64(sets[0]["out"])
-
-    skip = set(x for x in args.skip.split(",") if x)
-    rows = []
-
-    def report(stage, tiles, us, ok, nbytes):
-        row = {"stage": stage, "tiles": tiles, "us": round(us, 3), "tbs": round(nbytes / (us * 1e-6) / 1e12, 4),
-               "ok": ok}
-        rows.append(row)
-        print(json.dumps(row), flush=True)
-
-    def try_tiles(stage, tiles, calls_fn, ref, which, nbytes):
-        try:
-            calls = calls_fn(tiles)
-        except da.DecodeAttnError:
-            return None  # outside the ranges this shape allows
-        us = time_calls(calls)
-        calls[0]()
-        torch.cuda.synchronize()
-        ok = not differs(bf16_to_f64(sets[0][which]), ref)
-        report(stage, tiles, us, ok, nbytes)
-        return us if ok else None
-
-    kv_bytes = 2 * 2 * s.num_kv_heads * s.head_dim * int(np.sum(seq_lens))
-    best_attn, best_attn_us = {}, try_tiles("attn", {}, attn_calls, ref_flat, "flat", kv_bytes)
-    if "attn" not in skip:
-        for w, d in itertools.product(_parse_list(args.attn_wgs), _parse_list(args.attn_depth)):
-            t = {"attn_workgroups": w, "attn_depth": d}
-            us = try_tiles("attn", t, attn_calls, ref_flat, "flat", kv_bytes)
-            if us is not None and us < best_attn_us:
-                best_attn, best_attn_us = t, us
-
-    two = dict(best_attn, step_mode=2)
-    best_proj, best_proj_us = two, try_tiles("proj", two, step_calls, ref_out, "out", alg_bytes)
-    if "proj" not in skip:
-        for tn, ks in itertools.product(_parse_list(args.tile_n), _parse_list(args.ksplit)):
-            t = dict(two, proj_tile_n=tn, proj_ksplit=ks)
-            us = try_tiles("proj", t, step_calls, ref_out, "out", alg_bytes)
-            if us is not None and (best_proj_us is None or us < best_proj_us):
-                best_proj, best_proj_us = t, us
-
-    best, best_us = best_proj, best_proj_us
-    plan = da.decode_attn_plan(da.make_shape(s.batch, s.num_q_heads, s.num_kv_heads, s.max_seq_len, s.hidden, s.head_dim))
-    if "mode" not in skip and plan.fused:
-        # the single-launch step: attention workgroups aimed at x projection column tile
-        for w, tn in itertools.product([0] + _parse_list(args.step_wgs), [0, 128, 256, 512]):
-            t = {"step_mode": 1, "attn_workgroups": w, "proj_tile_n": tn}
-            us = try_tiles("mode", t, step_calls, ref_out, "out", alg_bytes)
-            if us is not None and us < best_us:
-                best, best_us = t, us
-    builtin_us = try_tiles("builtin", {}, step_calls, ref_out, "out", alg_bytes)
-    shape = {"batch": s.batch, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
-             "max_seq_len": s.max_seq_len, "hidden": s.hidden, "head_dim": s.head_dim}
-    print(json.dumps({"workload": wl.name, "best": best, "best_us": round(best_us, 3),
-                      "builtin_us": None if builtin_us is None else round(builtin_us, 3), "shape": shape}),
-          flush=True)
-    if args.emit:
-        emit_entry(args.table, shape, best, "%s: %.2f us (built-in %s us)" % (
-            wl.name, best_us, "?" if builtin_us is None else "%.2f" % builtin_us))
+    if args.mode == "search":
+        run_search(args)
+    else:
+        run_rules(args)
 
 
 if __name__ == "__main__":

@@ -55,10 +55,11 @@ struct TileEntry {
   decode_attn_tiles_t tiles;
 };
 constexpr TileEntry kTileTable[] = {
-#define TILE_ENTRY(b, hq, hkv, d, lmax, n, w, dp, tn, ks, mode) {b, hq, hkv, d, lmax, n, {w, dp, tn, ks, mode}},
+#define TILE_ENTRY(b, hq, hkv, d, lmax, n, w, dp, tn, ks, mode, cost, delay) \
+  {b, hq, hkv, d, lmax, n, {w, dp, tn, ks, mode, 0, cost, delay}},
 #include "tile_table.inc"
 #undef TILE_ENTRY
-    {0, 0, 0, 0, 0, 0, {0, 0, 0, 0, 0}},  // end of the table
+    {0, 0, 0, 0, 0, 0, {0, 0, 0, 0, 0, 0, 0, 0}},  // end of the table
 };
 
 // The shape a call runs with: the caller's, plus the table's tiles for its

@@ -292,8 +292,11 @@ def _table_rows():
 
 
 def test_measured_tile_table_rows_are_valid_and_used(lib):
-    fields = ("attn_workgroups", "attn_depth", "proj_tile_n", "proj_ksplit", "step_mode")
+    from decode_attention_output_amd import autotune
+
+    fields = autotune.TILE_FIELDS
     for row in _table_rows():
+        assert len(row) == 6 + len(fields), row
         shape = dict(batch=row[0], num_q_heads=row[1], num_kv_heads=row[2], head_dim=row[3], max_seq_len=row[4],
                      hidden=row[5])
         tiles = dict(zip(fields, row[6:]))

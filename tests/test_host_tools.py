@@ -34,8 +34,59 @@ def test_emit_entry_inserts_replaces_and_sorts(tmp_path):
     keys = [tuple(int(v) for v in r[len("TILE_ENTRY("):r.index(")")].split(",")[:6]) for r in rows]
     assert keys == sorted(keys) and len(set(keys)) == len(keys)
     mine = [r for r in rows if r.startswith("TILE_ENTRY(64, 8, 1, 128, 100, 512,")]
-    assert mine == ["TILE_ENTRY(64, 8, 1, 128, 100, 512, 64, 0, 0, 0, 0)  // replaced\n"]
-    assert "TILE_ENTRY(2, 8, 1, 256, 100, 512, 0, 0, 128, 0, 0)  // second\n" in rows
+    assert mine == ["TILE_ENTRY(64, 8, 1, 128, 100, 512, 64, 0, 0, 0, 0, 0, 0)  // replaced\n"]
+    assert "TILE_ENTRY(2, 8, 1, 256, 100, 512, 0, 0, 128, 0, 0, 0, 0)  // second\n" in rows
+    # a row carries every field of the table, in the table's order; None removes the row
+    autotune.emit_entry(str(table), small, {"attn_seq_cost": 3, "step_weight_delay": 50}, "all")
+    assert "TILE_ENTRY(2, 8, 1, 256, 100, 512, 0, 0, 0, 0, 0, 3, 50)  // all\n" in _rows(table)
+    autotune.emit_entry(str(table), small, None, "")
+    assert not [r for r in _rows(table) if r.startswith("TILE_ENTRY(2, 8, 1, 256, 100, 512,")]
+    assert len(_rows(table)) == n0 + 1
+
+
+def test_tile_fields_follow_the_table_macro():
+    # the table's row holds the shape, then the override fields in TILE_FIELDS order
+    src = open(os.path.join(ROOT, "decode_attention_output_amd", "csrc", "abi.hip")).read()
+    macro = src[src.index("#define TILE_ENTRY("):]
+    args = [a.strip() for a in macro[len("#define TILE_ENTRY("):macro.index(")")].split(",")]
+    assert len(args) == 6 + len(autotune.TILE_FIELDS)
+    # the macro's body lists the decode_attn_tiles_t fields in order: a field the table sets takes
+    # its argument, the others 0
+    body = macro[macro.index("{", macro.index(")")):]
+    body = body[body.index("{", 1) + 1:body.index("}")]
+    values = [v.strip() for v in body.split(",")]
+    struct = [n for n, _ in da.DecodeAttnTiles._fields_]
+    assert len(values) == len(struct)
+    for name, v in zip(struct, values):
+        want = args[6 + autotune.TILE_FIELDS.index(name)] if name in autotune.TILE_FIELDS else "0"
+        assert v == want, (name, v, want)
+
+
+def test_significance_needs_a_gap_beyond_the_spread():
+    T = autotune.Timing
+    builtin = T([10.0, 10.2, 10.1])
+    assert autotune.significant(T([9.5, 9.6, 9.55]), builtin)
+    assert not autotune.significant(T([9.95, 10.0, 9.9]), builtin)       # faster, but inside the noise
+    assert not autotune.significant(T([9.0, 10.5, 9.1]), builtin)        # its own spread swallows the gap
+    assert builtin.median == 10.1 and abs(builtin.spread - 0.2) < 1e-12
+
+
+def test_rule_selection_by_geometric_mean():
+    T = autotune.Timing
+    base = {"a": T([10.0]), "b": T([100.0]), "c": T([1.0])}
+    times = {
+        None: base,
+        "fast_on_big": {"a": T([10.0]), "b": T([50.0]), "c": T([1.5])},    # ratios 1, 0.5, 1.5
+        "even": {"a": T([9.0]), "b": T([90.0]), "c": T([0.9])},            # 0.9 on every shape
+        "partial": {"a": T([1.0]), "b": T([1.0])},                         # not allowed on c: left out
+    }
+    best, ratios = autotune.select_rule(times)
+    assert best == "even"
+    assert abs(ratios["fast_on_big"] - (0.75) ** (1 / 3)) < 1e-12 and "partial" not in ratios
+    assert ratios[None] == 1.0
+    # with nothing better the built-in choice stays
+    best, _ = autotune.select_rule({None: base, "slow": {k: T([v.median * 1.1]) for k, v in base.items()}})
+    assert best is None
 
 
 def test_bench_refuses_more_than_one_gpu():

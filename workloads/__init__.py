@@ -98,9 +98,22 @@ WIDE = DecodeWorkload("decode_b4_h16kv2_d256_L16384_o4096", DecodeShape(4, 16, 2
 PROMPT = PrefillWorkload("prefill_b1_t2048_h32kv8_ctx2048", 1, 2048, 32, 8, 128, 2048, seed=6)
 CHUNK = PrefillWorkload("prefill_b4_t512_h32kv8_ctx8192", 4, 512, 32, 8, 128, 8192, seed=7)
 
+# One GPU's share of the step when the decode workloads are spread over 8
+# GPUs: a kv head per GPU with the projection split by its input rows (each GPU
+# then adds its partial output into the others'), and an eighth of the batch.
+# They are not benchmarked; the tile search weighs its built-in rules over them.
+SHARE_PAGES_TP8 = DecodeWorkload("decode_b1_h4kv1_L2048_o4096", DecodeShape(1, 4, 1, 128, 2048, 4096), seed=8,
+                                 seq_len=2048)
+SHARE_LONG_TP8 = DecodeWorkload("decode_b4_h8kv1_L32768_o8192", DecodeShape(4, 8, 1, 128, 32768, 8192), seed=9,
+                                seq_len=32768)
+SHARE_BATCHED_DP8 = DecodeWorkload("decode_b2_h32kv8_ragged1024-8192_o4096", DecodeShape(2, 32, 8, 128, 8192, 4096),
+                                   seed=10, ragged=(1024, 8192))
+SHARES = [SHARE_PAGES_TP8, SHARE_LONG_TP8, SHARE_BATCHED_DP8]
+
 ALL = [TINY, PAGES, GEMM, BATCHED, LONG, WIDE, PROMPT, CHUNK]
-BY_NAME = {w.name: w for w in ALL}
+BY_NAME = {w.name: w for w in ALL + SHARES}
 DECODE = [TINY, PAGES, BATCHED, LONG, WIDE]
+RULE_SHAPES = [PAGES, BATCHED, LONG, WIDE] + SHARES
 PREFILL = [PROMPT, CHUNK]
 
 
