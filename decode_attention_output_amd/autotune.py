@@ -10,22 +10,26 @@ mean. This tool does both on the GPU through the C ABI's tile override
 
   search   one shape: attention tiles (stream-K workgroups x pipeline depth x
            the per-sequence charge), then projection tiles (column tile x K
-           split) with two launches, then the single-launch step's own knobs,
-           against the built-in choice. With --emit the winner becomes the
-           shape's row of the measured tile table (csrc/tile_table.inc) only if
-           it beats the built-in choice by more than the repeat spread of the
-           two (otherwise the row is removed: the built-in rules serve it).
+           split) on top of the best of them, or the small single-launch
+           step's own knobs, each timed as the whole step against the built-in
+           choice. The winner is timed once more in alternation with the
+           built-in choice; with --emit it becomes the shape's row of the
+           measured tile table (csrc/tile_table.inc) only if it beats the
+           built-in choice by more than the repeat spread of the two, and
+           otherwise the shape's row is removed (the built-in rules serve it).
   rules    candidate settings applied to every shape of a set (by default the
            benchmarked decode workloads and the one-GPU shares of a sharded
            step); each candidate's time is divided by the built-in time of the
            same shape, and the candidate with the best geometric mean of those
            ratios is reported as the rule to build in.
 
-Every candidate is timed over rotated copies of the inputs (at least 512 MiB,
-twice the Infinity Cache) with HIP events on one stream; a measurement is the
-median of several repeats, its spread the difference between the slowest and
-the fastest repeat. Every candidate's output is compared with the built-in
-choice's (two correct results differ by at most a couple of bf16 ulps).
+"Built-in choice" means the library's rules alone: an override whose fields
+are all zero bypasses the measured table as well. Every candidate is timed over
+rotated copies of the inputs (at least 512 MiB, twice the Infinity Cache) with
+HIP events on one stream; a measurement is the median of several repeats, its
+spread the difference between the slowest and the fastest repeat. Every
+candidate's output is compared with the built-in choice's (two correct results
+differ by at most a couple of bf16 ulps).
 
     python -m decode_attention_output_amd.autotune search --workload decode_b4_h64kv8_L32768_o8192 --emit
     python -m decode_attention_output_amd.autotune rules
@@ -153,62 +157,65 @@ class Bench:
         for r in range(R):
             st = {n: (t if r == 0 else t.clone()) for n, t in base.items()}
             st["out"] = torch.empty((s.batch, s.hidden), dtype=torch.bfloat16, device=dev)
-            st["flat"] = torch.empty((s.batch, s.o_in), dtype=torch.bfloat16, device=dev)
             st["ws"] = da.Workspace(dev)
             self.sets.append(st)
         self.stream = torch.cuda.Stream()
         torch.cuda.synchronize()
-        self.ref = {}
-        self.ref["flat"] = self._run_ref(self.attn_calls(None), "flat")
-        self.ref["out"] = self._run_ref(self.step_calls(None), "out")
-
-    def _run_ref(self, calls, which):
-        calls[0]()
-        self.torch.cuda.synchronize()
-        return self.bf16_to_f64(self.sets[0][which])
+        self.step_calls(None)[0]()
+        torch.cuda.synchronize()
+        self.ref = self.bf16_to_f64(self.sets[0]["out"])
 
     def bf16_to_f64(self, t):
         torch, np = self.torch, self.np
         return torch.from_numpy(t.cpu().view(torch.int16).numpy()).view(torch.bfloat16).double().numpy()
-
-    def attn_calls(self, tiles):
-        da = self.da
-        return [da.AttentionStep(st["q"], st["k"], st["v"], self.sl, out=st["flat"], workspace=st["ws"],
-                                 stream=self.stream, tiles=tiles) for st in self.sets]
 
     def step_calls(self, tiles):
         da = self.da
         return [da.DecodeStep(st["q"], st["k"], st["v"], self.sl, st["o_weight"], out=st["out"], workspace=st["ws"],
                               stream=self.stream, tiles=tiles) for st in self.sets]
 
-    def time(self, calls):
+    def _once(self, calls):
         torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for i in range(self.launches):
+            calls[i % len(calls)]()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / self.launches
+
+    def _warm(self, calls):
         for i in range(max(20, len(calls))):
             calls[i % len(calls)]()
-        torch.cuda.synchronize()
-        res = []
-        for _ in range(self.repeats):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(self.stream)
-            for i in range(self.launches):
-                calls[i % len(calls)]()
-            e1.record(self.stream)
-            torch.cuda.synchronize()
-            res.append(e0.elapsed_time(e1) * 1e3 / self.launches)
-        return Timing(res)
+        self.torch.cuda.synchronize()
 
-    def try_tiles(self, tiles, which="out"):
-        """Timing of the step (which="out") or of the attention alone (which="flat") under `tiles`,
-        or None if the tiles are outside what the shape allows or change the result."""
+    def time(self, calls):
+        self._warm(calls)
+        return Timing(self._once(calls) for _ in range(self.repeats))
+
+    def time_pair(self, calls_a, calls_b, rounds):
+        """Both call lists timed in alternation (a, b, a, b, ...), so that a drift of the clock
+        or the temperature over the measurement falls on both alike."""
+        self._warm(calls_a)
+        self._warm(calls_b)
+        ta, tb = [], []
+        for _ in range(rounds):
+            ta.append(self._once(calls_a))
+            tb.append(self._once(calls_b))
+        return Timing(ta), Timing(tb)
+
+    def try_tiles(self, tiles):
+        """Timing of the step under `tiles`, or None if the tiles are outside what the shape
+        allows or change the result."""
         np = self.np
         try:
-            calls = self.step_calls(tiles) if which == "out" else self.attn_calls(tiles)
+            calls = self.step_calls(tiles)
         except self.da.DecodeAttnError:
             return None
         t = self.time(calls)
         calls[0]()
         self.torch.cuda.synchronize()
-        got, ref = self.bf16_to_f64(self.sets[0][which]), self.ref[which]
+        got, ref = self.bf16_to_f64(self.sets[0]["out"]), self.ref
         err = np.abs(got - ref)
         if not np.all(np.isfinite(got)) or (err > 2.0 ** -6 * np.maximum(np.abs(ref), 1e-2)).any():
             return None
@@ -232,7 +239,7 @@ def parse(argv=None):
         p.add_argument("--min-rotate-mib", type=float, default=512.0)
     s = sub.choices["search"]
     s.add_argument("--workload", required=True)
-    s.add_argument("--attn-wgs", default="128,160,192,224,256,384")
+    s.add_argument("--attn-wgs", default="128,144,160,176,192,224,256")
     s.add_argument("--attn-depth", default="1,2")
     s.add_argument("--seq-cost", default="1,3,6,12")
     s.add_argument("--tile-n", default="64,128,256,512")
@@ -276,14 +283,15 @@ def run_search(args):
     best, best_t = {}, builtin
     plan = da.decode_attn_plan(da.make_shape(**b.shape()))
     if "attn" not in skip and plan.fused != 1:
-        base_attn = report("attn", {}, b.try_tiles({}, "flat"))
-        best_a, best_at = {}, base_attn
+        # attention tiles timed in the whole step: in the single-launch step the projection's
+        # workgroups share the chip with the attention's, so the attention alone misleads
+        best_a = {}
         for w, d, c in itertools.product(_parse_list(args.attn_wgs), _parse_list(args.attn_depth),
                                          _parse_list(args.seq_cost)):
             t = {"attn_workgroups": w, "attn_depth": d, "attn_seq_cost": c}
-            tm = report("attn", t, b.try_tiles(t, "flat"))
-            if tm is not None and tm.median < best_at.median:
-                best_a, best_at = t, tm
+            tm = report("attn", t, b.try_tiles(t))
+            if tm is not None and tm.median < best_t.median:
+                best, best_t, best_a = t, tm, t
         for tn, ks in itertools.product(_parse_list(args.tile_n), _parse_list(args.ksplit)):
             t = dict(best_a, proj_tile_n=tn, proj_ksplit=ks)
             tm = report("proj", t, b.try_tiles(t))
@@ -297,9 +305,9 @@ def run_search(args):
             if tm is not None and tm.median < best_t.median:
                 best, best_t = t, tm
     # the winner again, beside the built-in choice, so that both spreads come from the same moment
-    final_best = b.try_tiles(best) if best else builtin
-    final_builtin = b.try_tiles({})
-    keep = bool(best) and final_best is not None and significant(final_best, final_builtin)
+    # the winner once more, in alternation with the built-in choice
+    final_best, final_builtin = b.time_pair(b.step_calls(best), b.step_calls({}), 2 * args.repeats + 1)
+    keep = bool(best) and significant(final_best, final_builtin)
     summary = {"workload": wl.name, "best": best, "best_timing": final_best.as_dict(),
                "builtin_timing": final_builtin.as_dict(), "significant": keep, "shape": b.shape()}
     print(json.dumps(summary), flush=True)

@@ -22,11 +22,13 @@ namespace {
 
 using da::kHeadDim;
 
-// Stream-K attention workgroups: 192, three quarters of the compute units.
-// Measured over 128..768 on the ragged 16-sequence and the 4 x 32768-key
-// steps: 192 is about 1 % faster than 256 (one per compute unit) on both,
-// fewer is slower, and more only adds pieces to merge.
-constexpr int kAttnWorkgroups = 192;
+// Stream-K attention workgroups: 176 (22 per XCD), about two thirds of the
+// compute units. Chosen by the geometric mean of the step time over the
+// ragged 16-sequence, 4 x 32768-key and head_dim 256 steps and one-GPU shares
+// of them (112..256 tried): the projection workgroups of the single-launch
+// step then find free compute units to start their weight stream early, which
+// gains 2-4 % over 192 on the long steps; 128 and fewer leave HBM idle.
+constexpr int kAttnWorkgroups = 176;
 constexpr int kMaxAttnWorkgroups = 1024;    // largest stream-K grid a tile override may ask for
 constexpr int kAttnBlockKeys = 32;          // keys per wave step
 // Virtual 32-key blocks a stream-K workgroup is charged for starting a
@@ -220,7 +222,8 @@ constexpr size_t kStepMaxKvBytes = 64ull << 20;
 constexpr size_t kStepMaxWeightBytes = 64ull << 20;
 constexpr int kStepMaxBatch = 2;          // projection rows held per lane (four spill registers)
 constexpr int kStepResident = 512;        // workgroups resident at once: two 256-thread ones per CU
-constexpr int kStepAttnTarget = 128;      // attention workgroups aimed at
+constexpr int kStepAttnTarget = 192;      // attention workgroups aimed at (5 % faster than 128 on two
+                                          // ragged sequences of 8 kv heads; shorter steps have fewer pieces)
 constexpr int kStepMaxAttn = 384;         // at most, leaving room for the projection
 constexpr int kPieceGrain = 128;          // keys of a piece: a multiple of 4 waves x 32 keys
 struct StepPlan {
@@ -327,7 +330,9 @@ Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
     // the large single-launch step: the two-launch layout plus per-kv-head ready counters
     L.ready_counter0 = (int)align_up((size_t)counters, da::kCounterStride);
     const int ready_end = L.ready_counter0 + s->num_kv_heads * da::kStepReplicas * da::kCounterStride;
+    // (its attention keeps one 32-key step in flight per wave: a deeper pipeline runs in two launches)
     L.large = one_launch && !L.fused && L.proj.path == 1 && L.proj.mtiles <= 2 && s->head_dim == kHeadDim &&
+              L.attn.depth <= 1 &&
               !(s->flags & DA_FLAG_DEBUG_SCORES) && ready_end <= da::kStepCounterBase;
   }
   L.total = off;

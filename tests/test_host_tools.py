@@ -96,15 +96,17 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_attention_only_workspace_covers_the_table_row():
-    # the head_dim 256 row of the table sets the stream-K grid; an attention-only call (whose
-    # hidden size is not part of the lookup) must fit the workspace the size query reports
-    shape = dict(batch=4, num_q_heads=16, num_kv_heads=2, max_seq_len=16384, head_dim=256)
-    rows = [r for r in _rows(autotune.TABLE) if r.startswith("TILE_ENTRY(4, 16, 2, 256, 16384,")]
-    assert rows, "the table holds the head_dim 256 workload's row"
-    w = int(rows[0][len("TILE_ENTRY("):].split(",")[6])
-    need_attn = da.decode_attn_workspace_size(da.make_shape(hidden=8, tiles=dict(attn_workgroups=w), **shape))
-    assert da.decode_attn_workspace_size(da.make_shape(hidden=8, **shape)) >= need_attn
+def test_attention_only_workspace_covers_the_table_rows():
+    # a table row can set the attention grid; an attention-only call (whose hidden size is not part
+    # of the lookup, so it takes the row of the same attention shape) must fit the workspace that
+    # the size query of the full step reports
+    rows = [[int(v) for v in r[len("TILE_ENTRY("):r.index(")")].split(",")] for r in _rows(autotune.TABLE)]
+    assert rows
+    for row in rows:
+        shape = dict(batch=row[0], num_q_heads=row[1], num_kv_heads=row[2], head_dim=row[3], max_seq_len=row[4])
+        tiles = dict(zip(autotune.TILE_FIELDS, row[6:]))
+        need_attn = da.decode_attn_workspace_size(da.make_shape(hidden=8, tiles=tiles, **shape))
+        assert da.decode_attn_workspace_size(da.make_shape(hidden=row[5], **shape)) >= need_attn, row
 
 
 def test_mfma_summary_from_counter_and_trace_csvs(tmp_path, monkeypatch):
