@@ -33,6 +33,24 @@ def test_header_declares_the_binding_names():
     assert _declared_functions() == sorted(da.EXPORTED)
 
 
+def test_header_constants_match_the_binding():
+    # every integer #define of the header that the binding mirrors has the same value
+    text = open(os.path.join(ROOT, "include", "decode_attn.h")).read()
+    defines = {}
+    for line in text.splitlines():
+        parts = line.split(None, 2)
+        if len(parts) == 3 and parts[0] == "#define" and parts[1].startswith("DA_"):
+            value = parts[2].split("/*")[0].strip().replace("u", "")
+            try:
+                defines[parts[1]] = int(eval(value, {}))
+            except SyntaxError:
+                pass
+    mirrored = [n for n in defines if hasattr(da, n)]
+    assert {"DA_ERR_TIMEOUT", "DA_MAX_GROUP", "DA_FLAG_SEPARATE", "DA_HEAD_DIM_WIDE"} <= set(mirrored)
+    for name in mirrored:
+        assert getattr(da, name) == defines[name], name
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
