@@ -84,16 +84,18 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
       local += (L + kBlockKeys - 1) / kBlockKeys + cost;
     }
   }
-  s_scan[t] = local;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int v = t >= off ? s_scan[t - off] : 0;
-    __syncthreads();
-    s_scan[t] += v;
-    __syncthreads();
+  // inclusive scan of the threads' sums: within each wave by shuffles, then the wave totals
+  int inc = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
   }
+  if (lane == kWave - 1) s_scan[wave] = inc;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) inc += s_scan[w];
   {
-    int run = s_scan[t] - local;
+    int run = inc - local;
     for (int j = 0; j < per; ++j) {
       const int b = t * per + j;
       if (b < B) {
@@ -101,7 +103,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
         run += (s_len[b] + kBlockKeys - 1) / kBlockKeys + cost;
       }
     }
-    if (t == 0) s_pre[B] = s_scan[NT - 1];
+    if (t == NT - 1) s_pre[B] = inc;
   }
   __syncthreads();
 
