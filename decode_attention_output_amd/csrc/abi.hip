@@ -86,7 +86,7 @@ bool tiles_ok(const decode_attn_shape_t* s) {
   if (!t) return true;
   if (t->attn_workgroups < 0 || t->attn_workgroups > kMaxAttnWorkgroups) return false;
   if (t->attn_depth < 0 || t->attn_depth > 3) return false;
-  if (t->proj_ksplit < 0 || t->step_mode < 0 || t->step_mode > 2) return false;
+  if (t->proj_ksplit < 0 || t->step_mode < 0 || t->step_mode > 3) return false;
   if (t->step_wait_polls < 0 || t->step_wait_polls > (1 << 24)) return false;
   if (t->attn_seq_cost < 0 || t->attn_seq_cost > kMaxAttnSeqCost) return false;
   if (t->step_weight_delay < 0 || t->step_weight_delay > 1000) return false;
@@ -325,7 +325,7 @@ Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
       const size_t step_total =
           da::kCounterBlockBytes + L.step.part_o_bytes + L.step.part_ml_bytes + L.step.proj_part_bytes;
       off = std::max(off, step_total);
-      L.fused = one_launch;
+      L.fused = one_launch && !(t && t->step_mode == 3);
     }
     // the large single-launch step: the two-launch layout plus per-kv-head ready counters
     L.ready_counter0 = (int)align_up((size_t)counters, da::kCounterStride);

@@ -84,7 +84,9 @@ extern "C" {
  *  proj_ksplit      K-chunks the projection is cut into, >= 1 (rounded so that
  *                   every chunk is a whole number of the kernel's row batches)
  *  step_mode        0 built-in, 1 one launch where the single-launch step
- *                   supports the shape, 2 two launches (as DA_FLAG_SEPARATE)
+ *                   supports the shape, 2 two launches (as DA_FLAG_SEPARATE),
+ *                   3 the large single-launch step where it supports the shape
+ *                   (never the small one)
  *  step_wait_polls  bound of the single-launch steps' waits, in polls of a
  *                   counter, 1..2^24 (built-in 2^20, a fraction of a second);
  *                   a workgroup that reaches it gives up (decode_attn_step_status)

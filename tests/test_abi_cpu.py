@@ -250,7 +250,7 @@ def test_plan_one_launch_per_step(lib, cfg):
 
 @pytest.mark.parametrize("tiles", [dict(attn_workgroups=-1), dict(attn_workgroups=1025), dict(attn_depth=4),
                                    dict(attn_depth=-2), dict(proj_tile_n=96), dict(proj_tile_n=1024),
-                                   dict(proj_ksplit=-1), dict(step_mode=3), dict(step_wait_polls=-1),
+                                   dict(proj_ksplit=-1), dict(step_mode=4), dict(step_wait_polls=-1),
                                    dict(step_wait_polls=(1 << 24) + 1), dict(attn_seq_cost=-1),
                                    dict(attn_seq_cost=257)])
 def test_tile_override_out_of_range_is_a_shape_error(lib, tiles):
@@ -298,6 +298,8 @@ def test_tile_override_reaches_the_plan(lib):
     pages = dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=2048, hidden=4096)
     assert da.decode_attn_plan(da.make_shape(**pages)).fused == 1
     assert da.decode_attn_plan(da.make_shape(tiles=dict(step_mode=2), **pages)).fused == 0
+    # step_mode 3 asks for the large single-launch step, also where the small one would serve
+    assert da.decode_attn_plan(da.make_shape(tiles=dict(step_mode=3), **pages)).fused == 2
 
 
 def _table_rows():
