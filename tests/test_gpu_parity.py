@@ -489,6 +489,26 @@ def test_single_launch_large_step_matches_the_oracle_and_two_launches(gpu, case)
     np.testing.assert_array_equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("case", [(1, 32, 8, [2048], 2048, 4096), (2, 4, 1, [31, 700], 700, 512)],
+                         ids=lambda c: "B%d_H%d_KV%d_Lmax%d_N%d" % (c[0], c[1], c[2], c[4], c[5]))
+def test_large_step_chosen_for_a_small_shape(gpu, case):
+    # step_mode 3 runs the large single-launch step where the built-in choice is the small one
+    B, Hq, Hkv, sl, Lmax, hidden = case
+    assert da.decode_attn_plan(da.make_shape(B, Hq, Hkv, Lmax, hidden)).fused == 1
+    assert da.decode_attn_plan(da.make_shape(B, Hq, Hkv, Lmax, hidden, tiles=dict(step_mode=3))).fused == 2
+    inp = workloads.custom_decode_inputs(B, Hq, Hkv, sl, max_seq_len=Lmax, hidden=hidden, seed=B * 7 + Hq)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    s, w = dev_i32(inp["seq_lens"]), dev_bf16(inp["o_weight"])
+    ws = PoisonedWorkspace()
+    flat = host_words(da.decode_attn_only(q, k, v, s, workspace=ws))
+    large = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, tiles=dict(step_mode=3)))
+    _status_ok(ws, "large single launch on a small shape")
+    _counter_block_is_clear(ws)
+    two = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, separate=True))
+    _check_step(inp, {"flat": flat, "out": large}, what="large single launch on a small shape")
+    np.testing.assert_array_equal(large, two)
+
+
 def test_single_launch_large_step_timeout_is_reported(gpu):
     # projection workgroups allowed one poll give up while the attention of 16 x 8192 keys still runs
     B, Hq, Hkv, L, hidden = 16, 32, 8, 8192, 4096
