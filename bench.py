@@ -222,6 +222,14 @@ def bench_gemm(args, wl):
             launch(i)
     torch.cuda.synchronize()
 
+    # a plain elementwise copy of known size, outside the timed region: the HBM
+    # counters of a profiled run are scaled by what they read for it
+    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    torch.mul(calib_src, 1.0, out=calib_dst)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
+
     def run_steps(e0, e1, rotate):
         e0.record(stream)
         for i in range(args.steps):
@@ -450,15 +458,19 @@ def summarize_mfma(args):
     stem = re.sub(r"[^A-Za-z0-9]+", "_", kname).strip("_")
     out = os.path.join(PROFILES, "%s_%s_mfma.txt" % (stem, args.workload))
     os.makedirs(PROFILES, exist_ok=True)
+    tiles = getattr(args, "tiles", None)
+    extra = " --tiles '%s'" % tiles if tiles else ""
     with open(out, "w") as f:
         f.write("# rocprofv3 matrix-core summary: %s, workload %s\n" % (kname, args.workload))
         f.write("# commands (run from the repository root on one MI355X):\n")
         f.write("#   rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
-                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph\n" % args.workload)
+                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph%s\n" % (args.workload, extra))
         f.write("#   rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES "
                 "GRBM_GUI_ACTIVE --output-format csv -d <dir> -o mfma -- "
-                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph --steps 50\n" % args.workload)
-        f.write("#   python3 bench.py --workload %s --summarize-mfma '%s' <mfma csv> <stats csv>\n" % (args.workload, kname))
+                "python3 bench.py --workload %s --no-cpu-baseline --no-parity --no-graph%s --steps 50\n"
+                % (args.workload, extra))
+        f.write("#   python3 bench.py --workload %s%s --summarize-mfma '%s' <mfma csv> <stats csv>\n"
+                % (args.workload, extra, kname))
         f.write("# matrix-core busy %% = SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (trace duration x %.1f GHz x %d "
                 "SIMDs)\n" % (PEAK_CLOCK_GHZ, SIMDS))
         f.write("# executed matrix flops = (MOPS_F16 + MOPS_BF16) x 512, per dispatch\n")
