@@ -29,6 +29,7 @@
 namespace da {
 
 constexpr int kMergeBatch = 8;   // partials whose loads are in flight together in the merge
+constexpr int kWideLoads = 16;   // output loads in flight per thread in the merge of many partials
 
 // Block range [bound(i), bound(i+1)) of workgroup i of W over T blocks, and the
 // workgroup that owns block x. With T < W the first T workgroups take one
@@ -56,6 +57,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   constexpr int kWaveOut = GP * HD * 4;     // a wave's un-normalised output in its stage
   static_assert(kWaveOut + 2 * GP * 4 <= kStageBytes, "a wave's output fits its stage");
   static_assert(NT * 24 <= kStageBytes && NT * 4 <= kStageBytes, "merge scratch fits one stage");
+  static_assert(NT * 24 + 2 * GP * 4 <= NW * kStageBytes, "wide-merge scratch fits the stages");
   int* const s_pre = reinterpret_cast<int*>(smem);  // virtual blocks of the sequences before batch b (per kv head)
   int* const s_len = s_pre + kMaxAttnBatch + 1;
   char* const s_stage = smem + kAttnTableBytes;
@@ -192,8 +194,118 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
     return nstep > wave ? (nstep - wave + NW - 1) / NW : 0;
   };
 
+  // ---- the merge of more partials than one batch holds ----
+  // Every partial's running max and weight sum are read first (one per thread)
+  // and turned into per-query weights in LDS, so that the output loads of all
+  // partials can be requested together: two memory trips where batches of
+  // kMergeBatch take one trip each. The outputs are then added in partial
+  // order, each scaled by its weight (deterministic).
+  constexpr int kPairsPerThread = (GP * D4 + NT - 1) / NT;
+  constexpr int kWideBatch = kWideLoads / kPairsPerThread;
+  static_assert(kWideBatch >= 1, "at least one partial per batch");
+  auto merge_wide = [&](int b, int h, int slot0, int P) {
+    float* const w_f = s_cm;  // [P][G]: the partials' maxima, then their weights
+    float* const w_l = s_cl;  // [P][G]: the partials' weight sums
+    float* const w_M = reinterpret_cast<float*>(s_co + NT);  // [G]
+    float* const w_L = w_M + GP;                              // [G]
+    const int npairs = G * D4;
+    const int cnt = min(npairs, NT), nph = NT / cnt;  // threads per (query, 4 dims) pair
+    const int c = t % cnt, ph = t / cnt;
+    // this thread's partials: ph, ph + nph, ... (none if ph >= nph)
+    const int njp = ph < nph ? (P - ph + nph - 1) / nph : 0;
+    const uint32_t no_load = (uint32_t)p.part_o_bytes;  // beyond the range: reads 0
+    uint4 ov[kWideBatch][kPairsPerThread];
+    auto load_batch = [&](int jb) {
+#pragma unroll
+      for (int u = 0; u < kWideBatch; ++u)
+#pragma unroll
+        for (int pp = 0; pp < kPairsPerThread; ++pp) {
+          const int pr = c + pp * cnt, jj = jb + u;
+          const int g = pr / D4, d4 = pr % D4;
+          const uint32_t off = (jj < njp && pr < npairs)
+                                   ? ((uint32_t)((slot0 + ph + jj * nph) * G + g) * HD + d4 * 4) * 4
+                                   : no_load;
+          ov[u][pp] = rsrc_ld16_coherent(part_o, off);
+        }
+    };
+    uint2 ml = make_uint2(0u, 0u);
+    if (t < P * G) ml = rsrc_ld8_coherent(part_ml, (uint32_t)(slot0 * G + t) * 8);
+    load_batch(0);
+    if (t < P * G) {
+      w_f[t] = __builtin_bit_cast(float, ml.x);
+      w_l[t] = __builtin_bit_cast(float, ml.y);
+    }
+    __syncthreads();
+    if (t < G) {
+      float M = -INFINITY;
+#pragma unroll 8
+      for (int j = 0; j < P; ++j) M = fmaxf(M, w_f[j * G + t]);
+      float Ls = 0.f;
+#pragma unroll 8
+      for (int j = 0; j < P; ++j) {
+        const float m = w_f[j * G + t];
+        const float f = m == -INFINITY ? 0.f : exp2f(m - M);  // an empty partial weighs nothing
+        Ls = fmaf(f, w_l[j * G + t], Ls);
+        w_f[j * G + t] = f;
+      }
+      w_M[t] = M;
+      w_L[t] = Ls;
+    }
+    __syncthreads();
+    float acc[kPairsPerThread][4];
+#pragma unroll
+    for (int pp = 0; pp < kPairsPerThread; ++pp)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[pp][e] = 0.f;
+    for (int jb = 0; jb < njp; jb += kWideBatch) {
+      if (jb > 0) load_batch(jb);
+#pragma unroll
+      for (int u = 0; u < kWideBatch; ++u)
+#pragma unroll
+        for (int pp = 0; pp < kPairsPerThread; ++pp) {
+          const int pr = c + pp * cnt, jj = jb + u;
+          if (jj < njp && pr < npairs) {
+            const float f = w_f[(ph + jj * nph) * G + pr / D4];
+            acc[pp][0] = fmaf(f, __builtin_bit_cast(float, ov[u][pp].x), acc[pp][0]);
+            acc[pp][1] = fmaf(f, __builtin_bit_cast(float, ov[u][pp].y), acc[pp][1]);
+            acc[pp][2] = fmaf(f, __builtin_bit_cast(float, ov[u][pp].z), acc[pp][2]);
+            acc[pp][3] = fmaf(f, __builtin_bit_cast(float, ov[u][pp].w), acc[pp][3]);
+          }
+        }
+    }
+    auto write_pair = [&](int pr, const float (&o)[4]) {
+      const int g = pr / D4, d4 = pr % D4;
+      const int qh = h * G + g;
+      store4(b, qh, d4, o, 1.f / w_L[g]);
+      if (p.dbg_lse && d4 == 0) p.dbg_lse[(size_t)b * p.Hq + qh] = (w_M[g] + log2f(w_L[g])) * kLn2;
+    };
+    if (nph == 1) {
+#pragma unroll
+      for (int pp = 0; pp < kPairsPerThread; ++pp)
+        if (c + pp * cnt < npairs) write_pair(c + pp * cnt, acc[pp]);
+    } else {
+      // fewer pairs than threads: one pair per thread, the threads of a pair add up in order
+      s_co[t] = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+      __syncthreads();
+      if (t < cnt) {
+        float o[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int q2 = 0; q2 < nph; ++q2) {
+          const float4 v = s_co[t + q2 * cnt];
+          o[0] += v.x; o[1] += v.y; o[2] += v.z; o[3] += v.w;
+        }
+        write_pair(t, o);
+      }
+    }
+  };
+
+  // Merges of many partials wait until the range is done: only the first and
+  // the last piece of a range can be partial, and the last arriver of a
+  // sequence is nearly always at the end of its range. After the range the
+  // registers that the piece loop keeps are free for the merge's loads.
+  uint32_t wide_pending = 0;  // bit 0: the range's first piece waits for its merge, bit 1: its last piece
+
   // ---- the end of a piece: merge the waves, then write the sequence's output or store a partial ----
-  auto finish_piece = [&](const Piece& pc, AttnWaveT<HD>& aw) {
+  auto finish_piece = [&](const Piece& pc, AttnWaveT<HD>& aw, bool first_of_range) {
     const int b = pc.b, h = pc.h, seg = pc.seg;
     attn_wave_to_lds<GP, HD>(aw, s_o(wave), s_m(wave), s_l(wave), lane);
     __syncthreads();
@@ -242,58 +354,63 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
         // ---- the last piece merges the P partials at slots seg+first .. seg+last ----
         const int slot0 = seg + (int)first;
         const int npairs = G * D4;
-        for (int base = 0; base < npairs; base += NT) {
-          const int cnt = min(npairs - base, NT);
-          const int nph = NT / cnt;
-          const int pr = base + t % cnt, ph = t / cnt;
-          float M = -INFINITY, Ls = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
-          if (ph < nph) {
-            const int g = pr / D4, d4 = pr % D4;
-            for (int j0 = ph; j0 < P; j0 += kMergeBatch * nph) {
-              uint2 ml[kMergeBatch];
-              uint4 ov[kMergeBatch];
+        if (!kSignal && P > kMergeBatch && P * G <= NT) {
+          wide_pending |= first_of_range ? 1u : 2u;
+        } else {
+          for (int base = 0; base < npairs; base += NT) {
+            const int cnt = min(npairs - base, NT);
+            const int nph = NT / cnt;
+            const int pr = base + t % cnt, ph = t / cnt;
+            float M = -INFINITY, Ls = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
+            if (ph < nph) {
+              const int g = pr / D4, d4 = pr % D4;
+              for (int j0 = ph; j0 < P; j0 += kMergeBatch * nph) {
+                uint2 ml[kMergeBatch];
+                uint4 ov[kMergeBatch];
 #pragma unroll
-              for (int u = 0; u < kMergeBatch; ++u) {
-                const int j = j0 + u * nph;
-                const uint32_t sl = (uint32_t)((slot0 + min(j, P - 1)) * G + g);
-                ml[u] = rsrc_ld8_coherent(part_ml, sl * 8);
-                ov[u] = rsrc_ld16_coherent(part_o, (sl * HD + d4 * 4) * 4);
-              }
+                for (int u = 0; u < kMergeBatch; ++u) {
+                  const int j = j0 + u * nph;
+                  const uint32_t sl = (uint32_t)((slot0 + min(j, P - 1)) * G + g);
+                  ml[u] = rsrc_ld8_coherent(part_ml, sl * 8);
+                  ov[u] = rsrc_ld16_coherent(part_o, (sl * HD + d4 * 4) * 4);
+                }
 #pragma unroll
-              for (int u = 0; u < kMergeBatch; ++u) {
-                if (j0 + u * nph < P) {
-                  const float o[4] = {__builtin_bit_cast(float, ov[u].x), __builtin_bit_cast(float, ov[u].y),
-                                      __builtin_bit_cast(float, ov[u].z), __builtin_bit_cast(float, ov[u].w)};
-                  merge_partial(M, Ls, O, __builtin_bit_cast(float, ml[u].x), __builtin_bit_cast(float, ml[u].y), o);
+                for (int u = 0; u < kMergeBatch; ++u) {
+                  if (j0 + u * nph < P) {
+                    const float o[4] = {__builtin_bit_cast(float, ov[u].x), __builtin_bit_cast(float, ov[u].y),
+                                        __builtin_bit_cast(float, ov[u].z), __builtin_bit_cast(float, ov[u].w)};
+                    merge_partial(M, Ls, O, __builtin_bit_cast(float, ml[u].x), __builtin_bit_cast(float, ml[u].y), o);
+                  }
                 }
               }
             }
-          }
-          s_cm[t] = M;
-          s_cl[t] = Ls;
-          s_co[t] = make_float4(O[0], O[1], O[2], O[3]);
-          __syncthreads();
-          if (t < cnt) {
-            float Mf = -INFINITY, Lf = 0.f, Of[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int q2 = 0; q2 < nph; ++q2) {
-              const float4 o4 = s_co[t + q2 * cnt];
-              const float o[4] = {o4.x, o4.y, o4.z, o4.w};
-              merge_partial(Mf, Lf, Of, s_cm[t + q2 * cnt], s_cl[t + q2 * cnt], o);
+            s_cm[t] = M;
+            s_cl[t] = Ls;
+            s_co[t] = make_float4(O[0], O[1], O[2], O[3]);
+            __syncthreads();
+            if (t < cnt) {
+              float Mf = -INFINITY, Lf = 0.f, Of[4] = {0.f, 0.f, 0.f, 0.f};
+              for (int q2 = 0; q2 < nph; ++q2) {
+                const float4 o4 = s_co[t + q2 * cnt];
+                const float o[4] = {o4.x, o4.y, o4.z, o4.w};
+                merge_partial(Mf, Lf, Of, s_cm[t + q2 * cnt], s_cl[t + q2 * cnt], o);
+              }
+              const int g = pr / D4, d4 = pr % D4;
+              const int qh = h * G + g;
+              store4(b, qh, d4, Of, 1.f / Lf);
+              if (p.dbg_lse && d4 == 0) p.dbg_lse[(size_t)b * p.Hq + qh] = (Mf + log2f(Lf)) * kLn2;
             }
-            const int g = pr / D4, d4 = pr % D4;
-            const int qh = h * G + g;
-            store4(b, qh, d4, Of, 1.f / Lf);
-            if (p.dbg_lse && d4 == 0) p.dbg_lse[(size_t)b * p.Hq + qh] = (Mf + log2f(Lf)) * kLn2;
+            __syncthreads();
           }
-          __syncthreads();
+          signal_ready(h);
         }
-        signal_ready(h);
         DA_TRACE(4);
       }
     }
     __syncthreads();  // LDS is reused by the next piece
   };
 
+  const long x0 = x;
   while (x < xe) {
     const Piece pc = piece_at(x);
     if (pc.lb0 < pc.lb1) {
@@ -304,9 +421,19 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
       aw.reset();
       attn_wave_steps<GP, D, HD>(aw, qa, sg, pc.lb0 + wave, NW, wave_steps(pc), pc.L, s_stage + wave * kStageBytes,
                                  lane);
-      finish_piece(pc, aw);
+      finish_piece(pc, aw, x == x0);
     }
     x = min(xe, pc.se);
+  }
+  // the merges that waited: a partial piece is the range's first one or holds its last block
+#pragma unroll 1
+  for (int k = 0; k < 2; ++k) {
+    if (!(wide_pending & (1u << k))) continue;
+    const Piece pc = piece_at(k == 0 ? x0 : xe - 1);
+    const long first = range_owner(pc.rs, T, W), last = range_owner(pc.se - 1, T, W);
+    merge_wide(pc.b, pc.h, pc.seg + (int)first, (int)(last - first + 1));
+    signal_ready(pc.h);
+    __syncthreads();  // the merge scratch is reused
   }
   DA_TRACE(6);
 }
