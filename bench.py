@@ -271,12 +271,12 @@ def bench_gemm(args, wl):
         "config": {"workload": wl.name, "m": M, "n": N, "k": K, "flops": flops, "rotation_sets": R},
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_kernel",
+            "kernel": gemm_f16_kernel(M, N),
             "achieved": round(achieved, 3),
             "peak": MFMA_F16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 5),
-            "traffic": traffic_from_profile(wl.name, "gemm_kernel"),
+            "traffic": traffic_from_profile(wl.name, gemm_f16_kernel(M, N)),
             "avg_launch_us": round(gpu_us, 3),
             "flops_per_launch": flops,
             "timing": "HIP events around the timed back-to-back launches on the bench stream",
@@ -315,7 +315,13 @@ def bench_gemm(args, wl):
 
 
 KNOWN_KERNELS = ("decode_step_large_kernel", "decode_step_kernel", "attn_streamk_kernel", "gemm_kernel", "gemv_kernel",
-                 "prefill_kernel", "read_probe_kernel")
+                 "gemm_narrow_kernel", "prefill_kernel", "read_probe_kernel")
+
+
+def gemm_f16_kernel(m, n):
+    """The kernel gemm_f16 launches for an m x n product: 16 x 32 tiles over all of K when fewer
+    than 256 tiles of 128 columns x 16 rows would be launched, else the 128-column GEMM."""
+    return "gemm_narrow_kernel" if -(-n // 128) * (m // 16) < 256 else "gemm_kernel"
 
 
 def kernel_alg_bytes(args):
@@ -329,7 +335,8 @@ def kernel_alg_bytes(args):
     if isinstance(wl, workloads.PrefillWorkload):
         return {"prefill_kernel": prefill_alg_bytes(wl)}, "prefill_kernel"
     if isinstance(wl, workloads.GemmWorkload):
-        return {"gemm_kernel": 2 * (wl.m * wl.k + wl.k * wl.n + wl.m * wl.n)}, "gemm_kernel"
+        kname = gemm_f16_kernel(wl.m, wl.n)
+        return {kname: 2 * (wl.m * wl.k + wl.k * wl.n + wl.m * wl.n)}, kname
     s = wl.shape
     seq_lens = workloads.draw_seq_lens(wl, np.random.default_rng(wl.seed))
     tiles = json.loads(args.tiles) if args.tiles else None

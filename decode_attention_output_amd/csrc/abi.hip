@@ -745,7 +745,11 @@ int gemm_f16(const void* a, const void* b, void* c, int32_t M, int32_t N, int32_
   g.kchunk = K;
   g.ksplit = 1;
   g.mtiles = 1;
-  return da::launch_gemm_f16(g, (hipStream_t)stream) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+  // too few 128-column tiles to fill the chip: 16 x 32 tiles over all of K
+  const bool narrow = (long)ceil_div(N, da::kGemmTileN) * (M / 16) < da::kGemmNarrowBelow;
+  const hipError_t e = narrow ? da::launch_gemm_narrow_f16(g, (hipStream_t)stream)
+                              : da::launch_gemm_f16(g, (hipStream_t)stream);
+  return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
 int prefill_attn_fwd(const void* q, const void* k_cache, const void* v_cache, const int32_t* ctx_lens, void* out,

@@ -174,5 +174,9 @@ hipError_t launch_read_probe(const void* src, uint64_t bytes, uint32_t* sink, in
 hipError_t launch_gemv(const GemvParams& p, int mpad, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_f16(const GemmParams& p, hipStream_t s);
+// 16 x 32 output tiles over all of K, 512 threads (no workspace): for products whose 128-column tiles
+// would not fill the chip; M and N multiples of 16, K a multiple of 32.
+hipError_t launch_gemm_narrow_f16(const GemmParams& p, hipStream_t s);
+constexpr int kGemmNarrowBelow = 256;  // 128-column tiles below which the narrow tiles are used
 
 }  // namespace da

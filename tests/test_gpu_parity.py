@@ -115,6 +115,27 @@ def test_gemm_f16_all_ones_golden(gpu):
     assert np.all(c == 0x6400)  # every entry is exactly k = 1024
 
 
+GEMM_SHAPES = [
+    # (M, N, K): 16 x 32 tiles over all of K where 128-column tiles would not fill the chip
+    (16, 16, 32),       # one tile, half of it past N
+    (48, 80, 96),       # a ragged last column tile; three K-steps for four waves
+    (32, 1040, 2048),   # deep K: more K-steps per wave than are requested at once
+    (512, 1024, 64),    # 256 column tiles of 128: the wide tiles
+    (256, 4096, 32),    # the wide tiles, one K-step
+]
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES, ids=lambda c: "M%d_N%d_K%d" % c)
+def test_gemm_f16_integer_shapes_bit_exact(gpu, shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    a = rng.integers(-1, 1, endpoint=True, size=(M, K)).astype(np.float16).view(np.uint16)
+    b = rng.integers(-1, 1, endpoint=True, size=(K, N)).astype(np.float16).view(np.uint16)
+    c = da.gemm_f16(dev_f16(a), dev_f16(b))
+    ref, _ = oracle.gemm_f16(a, b)
+    np.testing.assert_array_equal(host_words(c), ref)
+
+
 # ---- edge cases of the attention path ------------------------------------
 
 EDGE = [

@@ -183,3 +183,13 @@ def test_traffic_summaries_for_every_kernel_of_the_run(tmp_path, monkeypatch):
     gfields = dict(l.split(" = ", 1) for l in (tmp_path / "profiles" / files[1]).read_text().splitlines()
                    if " = " in l and not l.startswith("#"))
     assert gfields["dominant"] == "False" and int(gfields["hbm_read_bytes_per_dispatch"]) == 500 * 512
+
+
+def test_gemm_f16_kernel_names_the_launched_kernel():
+    # the rule of gemm_f16: fewer than 256 tiles of 16 rows x 128 columns -> 16 x 32 tiles over all of K
+    import bench
+
+    assert bench.gemm_f16_kernel(256, 512) == "gemm_narrow_kernel"    # the fp16 check: 64 wide tiles
+    assert bench.gemm_f16_kernel(32, 1040) == "gemm_narrow_kernel"
+    assert bench.gemm_f16_kernel(512, 1024) == "gemm_kernel"          # 256 wide tiles
+    assert bench.gemm_f16_kernel(256, 4096) == "gemm_kernel"
