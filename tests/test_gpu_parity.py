@@ -47,6 +47,7 @@ def _run_step(inp, ws=None, scale=0.0, debug=False):
         dbg_s = torch.full((B, Hq, Lmax), float("nan"), dtype=torch.float32, device="cuda")
         dbg_l = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
         da.decode_attn_only(q, k, v, sl, workspace=ws, softmax_scale=scale, debug_scores=dbg_s, debug_lse=dbg_l)
+        _status_ok(ws, "debug scores")
         res["scores"] = dbg_s.cpu().numpy()
         res["lse"] = dbg_l.cpu().numpy()
     torch.cuda.synchronize()
