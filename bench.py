@@ -102,8 +102,9 @@ def dominant_kernel(wl, plan, seq_lens):
         + 2 * s.batch * s.o_in
     proj_bytes = 2 * s.o_in * s.hidden + 2 * s.batch * s.o_in + 2 * s.batch * s.hidden
     if plan.fused:
-        # one launch carries the whole step: the small single-launch step (1) or the large one (2)
-        name = "decode_step_kernel" if plan.fused == 1 else "decode_step_large_kernel"
+        # one launch carries the whole step: the small single-launch step (1), the large one (2)
+        # or the tiny one (3)
+        name = {1: "decode_step_kernel", 2: "decode_step_large_kernel", 3: "decode_step_tiny_kernel"}[plan.fused]
         return name, workloads_alg_bytes(s, seq_lens), "step"
     if proj_bytes >= attn_bytes:
         return ("gemv_kernel" if plan.oproj_path == 0 else "gemm_kernel"), proj_bytes, "oproj"
@@ -314,8 +315,8 @@ def bench_gemm(args, wl):
     print(json.dumps(result), flush=True)
 
 
-KNOWN_KERNELS = ("decode_step_large_kernel", "decode_step_kernel", "attn_streamk_kernel", "gemm_kernel", "gemv_kernel",
-                 "gemm_narrow_kernel", "prefill_kernel", "read_probe_kernel")
+KNOWN_KERNELS = ("decode_step_large_kernel", "decode_step_tiny_kernel", "decode_step_kernel", "attn_streamk_kernel",
+                 "gemm_kernel", "gemv_kernel", "gemm_narrow_kernel", "prefill_kernel", "read_probe_kernel")
 
 
 def gemm_f16_kernel(m, n):
@@ -347,7 +348,8 @@ def kernel_alg_bytes(args):
     attn = 2 * 2 * s.num_kv_heads * D * int(np.sum(seq_lens)) + 2 * s.batch * s.num_q_heads * D + 2 * s.batch * s.o_in
     proj = 2 * s.o_in * s.hidden + 2 * s.batch * s.o_in + 2 * s.batch * s.hidden
     whole = workloads.algorithmic_bytes(s, seq_lens)
-    return {"decode_step_large_kernel": whole, "decode_step_kernel": whole, "attn_streamk_kernel": attn,
+    return {"decode_step_large_kernel": whole, "decode_step_kernel": whole, "decode_step_tiny_kernel": whole,
+            "attn_streamk_kernel": attn,
             "gemm_kernel": proj, "gemv_kernel": proj, "read_probe_kernel": (whole + 15) // 16 * 16,
             kname: kbytes}, kname
 

@@ -282,7 +282,7 @@ def run_search(args):
     builtin = report("builtin", {}, b.try_tiles({}))
     best, best_t = {}, builtin
     plan = da.decode_attn_plan(da.make_shape(**b.shape()))
-    if "attn" not in skip and plan.fused != 1:
+    if "attn" not in skip and plan.fused not in (1, 3):
         # attention tiles timed in the whole step: in the single-launch step the projection's
         # workgroups share the chip with the attention's, so the attention alone misleads
         best_a = {}
@@ -297,7 +297,8 @@ def run_search(args):
             tm = report("proj", t, b.try_tiles(t))
             if tm is not None and tm.median < best_t.median:
                 best, best_t = t, tm
-    if "mode" not in skip and plan.fused == 1:
+    if "mode" not in skip and plan.fused in (1, 3):
+        # (a tiny step, fused 3, has no tiles of its own: the small step's are its alternatives)
         for w, tn, dl in itertools.product([0] + _parse_list(args.step_wgs), [0, 128, 256, 512],
                                            _parse_list(args.weight_delay)):
             t = {"step_mode": 1, "attn_workgroups": w, "proj_tile_n": tn, "step_weight_delay": dl}

@@ -86,7 +86,7 @@ bool tiles_ok(const decode_attn_shape_t* s) {
   if (!t) return true;
   if (t->attn_workgroups < 0 || t->attn_workgroups > kMaxAttnWorkgroups) return false;
   if (t->attn_depth < 0 || t->attn_depth > 3) return false;
-  if (t->proj_ksplit < 0 || t->step_mode < 0 || t->step_mode > 3) return false;
+  if (t->proj_ksplit < 0 || t->step_mode < 0 || t->step_mode > 4) return false;
   if (t->step_wait_polls < 0 || t->step_wait_polls > (1 << 24)) return false;
   if (t->attn_seq_cost < 0 || t->attn_seq_cost > kMaxAttnSeqCost) return false;
   if (t->step_weight_delay < 0 || t->step_weight_delay > 1000) return false;
@@ -292,6 +292,7 @@ struct Layout {
   bool fits;
   bool fused;  // decode_attn_fwd runs the single-launch step
   bool large;  // decode_attn_fwd runs the single-launch large step (stream-K attention + MFMA GEMM items)
+  bool tiny;   // decode_attn_fwd runs the tiny step (every workgroup computes the whole attention)
 };
 
 // Workspace: [arrival counters][attention partials][attention output][projection partials]
@@ -334,6 +335,13 @@ Layout layout_for(const decode_attn_shape_t* s, bool with_proj) {
     L.large = one_launch && !L.fused && L.proj.path == 1 && L.proj.mtiles <= 2 && s->head_dim == kHeadDim &&
               L.attn.depth <= 1 &&
               !(s->flags & DA_FLAG_DEBUG_SCORES) && ready_end <= da::kStepCounterBase;
+    // the tiny step: K/V small enough for every workgroup to compute the whole attention
+    const size_t kv_bytes = (size_t)s->batch * s->num_kv_heads * s->max_seq_len * s->head_dim * 2 * 2;
+    const int mode = t ? t->step_mode : 0;
+    L.tiny = one_launch && (mode == 0 || mode == 4) && s->head_dim == kHeadDim && s->batch <= da::kTinyMaxBatch &&
+             s->num_q_heads * s->head_dim <= da::kTinyMaxK && kv_bytes <= da::kTinyMaxKvBytes &&
+             !(s->flags & DA_FLAG_DEBUG_SCORES);
+    if (L.tiny) L.fused = L.large = false;
   }
   L.total = off;
   L.fits = counters <= da::kStepCounterBase && L.attn.part_o_bytes < (1ull << 32) &&
@@ -485,6 +493,27 @@ int run_step(const void* q, const void* k, const void* v, const int32_t* sl, con
   return da::launch_decode_step(p, sp.gpad, sp.mpad, sp.tile_n, st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
+// The tiny step: no workspace, no waits.
+int run_step_tiny(const void* q, const void* k, const void* v, const int32_t* sl, const void* w, void* out,
+                  const decode_attn_shape_t* s, hipStream_t st) {
+  da::StepTinyParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.seq_lens = sl;
+  p.w = (const uint16_t*)w;
+  p.out = (uint16_t*)out;
+  p.B = s->batch;
+  p.Hq = s->num_q_heads;
+  p.Hkv = s->num_kv_heads;
+  p.G = s->num_q_heads / s->num_kv_heads;
+  p.Lmax = s->max_seq_len;
+  p.N = s->hidden;
+  const float scale = s->softmax_scale != 0.f ? s->softmax_scale : 1.0f / sqrtf((float)kHeadDim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return da::launch_decode_step_tiny(p, pow2_at_least(p.G), st) == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
 // The single-launch large step: stream-K attention workgroups and the MFMA
 // GEMM items of the projection in one grid.
 int run_step_large(const da::AttnParams& attn, const void* w, void* out, const decode_attn_shape_t* s,
@@ -615,6 +644,7 @@ int fwd_impl(const void* q, const void* k_cache, const void* v_cache, const int3
   char* ws = (char*)shape->workspace;
   void* flat = ws + L.off_flat;
   const da::AttnParams p = attn_params(q, k_cache, v_cache, seq_lens, flat, shape, L);
+  if (L.tiny) return run_step_tiny(q, k_cache, v_cache, seq_lens, o_weight, out, shape, st);
   if (L.fused) return run_step(q, k_cache, v_cache, seq_lens, o_weight, out, shape, L, st);
   if (L.large) return run_step_large(p, o_weight, out, shape, L, st);
   if ((rc = run_attention(p, L, st))) return rc;
@@ -650,6 +680,19 @@ int decode_attn_plan(const decode_attn_shape_t* shape_in, decode_attn_plan_t* pl
   const int D = shape->head_dim;
   const int Ko = shape->num_q_heads * D;
   memset(plan, 0, sizeof *plan);
+  if (L.tiny) {
+    // one launch, every workgroup the whole attention (one piece per sequence) and 16 columns over all of K
+    const int wgs = ceil_div(shape->hidden, da::kTinyCols);
+    plan->qk = {G, kHeadDim, shape->max_seq_len, 16, kHeadDim, kAttnBlockKeys, 1, wgs};
+    plan->pv = {G, shape->max_seq_len, kHeadDim, 16, kAttnBlockKeys, kHeadDim, 1, wgs};
+    plan->oproj = {shape->batch, Ko, shape->hidden, shape->batch, Ko, da::kTinyCols, 1, wgs};
+    plan->split_len = shape->max_seq_len;
+    plan->num_splits = 1;
+    plan->oproj_path = 0;
+    plan->fused = 3;
+    plan->workspace_bytes = L.total;
+    return DA_OK;
+  }
   if (L.fused) {
     // one launch: a fixed number of pieces per sequence, projection tiles of whole kv heads
     const StepPlan& sp = L.step;

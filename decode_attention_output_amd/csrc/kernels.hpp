@@ -138,6 +138,25 @@ struct StepParams {
   float scale_log2;         // softmax scale * log2(e)
 };
 
+// The single-launch step for tiny steps: every workgroup computes the whole
+// attention itself (its K/V are a few hundred KiB at most) and then kTinyCols
+// output columns of the projection over all of K; no workspace, no hand-over.
+struct StepTinyParams {
+  const uint16_t* q;        // bf16 [B, Hq, 128]
+  const uint16_t* k;        // bf16 [B, Hkv, Lmax, 128]
+  const uint16_t* v;        // bf16 [B, Hkv, Lmax, 128]
+  const int32_t* seq_lens;  // [B]
+  const uint16_t* w;        // bf16 [Hq*128, N]
+  uint16_t* out;            // bf16 [B, N]
+  int B, Hq, Hkv, G, Lmax, N;
+  float scale_log2;         // softmax scale * log2(e)
+};
+constexpr int kTinyCols = 16;                    // output columns per workgroup
+constexpr int kTinyMaxK = 2048;                  // Hq * 128 at most
+constexpr int kTinyMaxBatch = 2;
+constexpr size_t kTinyMaxKvBytes = 256u << 10;   // K and V bytes of the whole step at most
+hipError_t launch_decode_step_tiny(const StepTinyParams& p, int gpad, hipStream_t s);
+
 // The single-launch large step: stream-K attention workgroups, then one
 // workgroup per MFMA GEMM item (ntiles column tiles x mgroups row groups x
 // gemm.ksplit K-chunks, K-chunk major).

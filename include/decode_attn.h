@@ -84,9 +84,10 @@ extern "C" {
  *  proj_ksplit      K-chunks the projection is cut into, >= 1 (rounded so that
  *                   every chunk is a whole number of the kernel's row batches)
  *  step_mode        0 built-in, 1 one launch where the single-launch step
- *                   supports the shape, 2 two launches (as DA_FLAG_SEPARATE),
- *                   3 the large single-launch step where it supports the shape
- *                   (never the small one)
+ *                   supports the shape (never the tiny one), 2 two launches
+ *                   (as DA_FLAG_SEPARATE), 3 the large single-launch step where
+ *                   it supports the shape (never the small one), 4 the tiny
+ *                   step where it supports the shape
  *  step_wait_polls  bound of the single-launch steps' waits, in polls of a
  *                   counter, 1..2^24 (built-in 2^20, a fraction of a second);
  *                   a workgroup that reaches it gives up (decode_attn_step_status)
@@ -181,6 +182,10 @@ typedef struct {
                            the stream-K attention workgroups, then the MFMA
                            projection's items, each of which requests its first
                            weight rows and waits for the kv heads of its K-chunk;
+                           3: one launch for tiny steps (head_dim 128, B <= 2,
+                           Hq*128 <= 2048, at most 256 KiB of K and V): every
+                           workgroup computes the whole attention itself and 16
+                           output columns over all of K; no workspace is used;
                            0: two launches                                         */
   size_t workspace_bytes;
 } decode_attn_plan_t;

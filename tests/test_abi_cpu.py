@@ -198,7 +198,11 @@ def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
     # the long axis (keys) is streamed 32 keys per wave step and cut evenly over the workgroups
     assert plan.qk.tile_n == 32 and plan.pv.tile_k == 32
     keys = cfg["batch"] * cfg["num_kv_heads"] * cfg["max_seq_len"]
-    if plan.fused == 1:
+    if plan.fused == 3:
+        # the tiny step: each workgroup streams every sequence whole (one piece), 16 columns each
+        assert plan.num_splits == 1 and plan.split_len == cfg["max_seq_len"]
+        assert plan.qk.workgroups == -(-cfg["hidden"] // 16)
+    elif plan.fused == 1:
         # one launch: every sequence cut into the same pieces of a multiple of 128 keys
         assert plan.split_len % 128 == 0 and plan.num_splits == -(-cfg["max_seq_len"] // plan.split_len)
         assert plan.qk.workgroups == cfg["batch"] * cfg["num_kv_heads"] * plan.num_splits
@@ -213,27 +217,29 @@ def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
         assert plan.qk.workgroups >= min(176, keys // 128)
         assert plan.split_len >= min(128, 32 * (-(-keys // 32)))
         assert plan.oproj.workgroups >= min(256, (cfg["hidden"] // 128) * (cfg["num_q_heads"] * 128 // 128))
-    # projection path: the small single-launch step's own VALU projection, else the MFMA GEMM at
-    # every batch (K = Hq*128), in the large single-launch step (fused 2) or a launch of its own
-    assert plan.oproj_path == (0 if plan.fused == 1 else 1)
+    # projection path: the single-launch small and tiny steps' own VALU projections, else the MFMA
+    # GEMM at every batch (K = Hq*128), in the large single-launch step (fused 2) or a launch of its own
+    assert plan.oproj_path == (0 if plan.fused in (1, 3) else 1)
     assert plan.workspace_bytes == da.decode_attn_workspace_size(da.make_shape(**cfg))
 
 
-SMALL = [dict(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=256, hidden=512),
-         dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=2048, hidden=4096),
-         dict(batch=2, num_q_heads=16, num_kv_heads=2, max_seq_len=128, hidden=256)]
+TINY = [dict(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=256, hidden=512),
+        dict(batch=2, num_q_heads=16, num_kv_heads=2, max_seq_len=128, hidden=256)]
+SMALL = [dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=2048, hidden=4096),
+         dict(batch=2, num_q_heads=16, num_kv_heads=2, max_seq_len=256, hidden=256)]
 LARGE = [dict(batch=3, num_q_heads=16, num_kv_heads=2, max_seq_len=128, hidden=256),
          dict(batch=16, num_q_heads=32, num_kv_heads=8, max_seq_len=8192, hidden=4096),
          dict(batch=4, num_q_heads=64, num_kv_heads=8, max_seq_len=32768, hidden=8192)]
 
 
-@pytest.mark.parametrize("cfg", SMALL + LARGE)
+@pytest.mark.parametrize("cfg", TINY + SMALL + LARGE)
 def test_plan_one_launch_per_step(lib, cfg):
-    # small steps: the single-launch step with its own projection (fused 1); larger ones: the
-    # stream-K attention and the MFMA projection's items in one grid (fused 2)
+    # tiny steps (at most 256 KiB of K and V): every workgroup computes the whole attention
+    # (fused 3); small steps: the single-launch step with its own projection (fused 1); larger
+    # ones: the stream-K attention and the MFMA projection's items in one grid (fused 2)
     plan = da.decode_attn_plan(da.make_shape(**cfg))
     sep = da.decode_attn_plan(da.make_shape(flags=da.DA_FLAG_SEPARATE, **cfg))
-    assert plan.fused == (1 if cfg in SMALL else 2)
+    assert plan.fused == (3 if cfg in TINY else 1 if cfg in SMALL else 2)
     assert sep.fused == 0
     # the workspace does not depend on the launch choice
     assert plan.workspace_bytes == sep.workspace_bytes
@@ -246,11 +252,15 @@ def test_plan_one_launch_per_step(lib, cfg):
         # every workgroup of the single launch is resident at once (two per compute unit)
         assert plan.qk.workgroups + plan.oproj.workgroups <= 512
         assert plan.oproj_path == 0 and plan.oproj.tile_n in (128, 256, 512)
+    if plan.fused == 3:
+        # one piece per sequence, 16 output columns over all of K per workgroup
+        assert plan.num_splits == 1 and plan.oproj.tile_n == 16 and plan.oproj.split == 1
+        assert plan.oproj.workgroups == -(-cfg["hidden"] // 16) == plan.qk.workgroups
 
 
 @pytest.mark.parametrize("tiles", [dict(attn_workgroups=-1), dict(attn_workgroups=1025), dict(attn_depth=4),
                                    dict(attn_depth=-2), dict(proj_tile_n=96), dict(proj_tile_n=1024),
-                                   dict(proj_ksplit=-1), dict(step_mode=4), dict(step_wait_polls=-1),
+                                   dict(proj_ksplit=-1), dict(step_mode=5), dict(step_wait_polls=-1),
                                    dict(step_wait_polls=(1 << 24) + 1), dict(attn_seq_cost=-1),
                                    dict(attn_seq_cost=257)])
 def test_tile_override_out_of_range_is_a_shape_error(lib, tiles):
@@ -300,6 +310,12 @@ def test_tile_override_reaches_the_plan(lib):
     assert da.decode_attn_plan(da.make_shape(tiles=dict(step_mode=2), **pages)).fused == 0
     # step_mode 3 asks for the large single-launch step, also where the small one would serve
     assert da.decode_attn_plan(da.make_shape(tiles=dict(step_mode=3), **pages)).fused == 2
+    # step_mode 4 asks for the tiny step; where the K/V are too large for it, the built-in choice stays
+    assert da.decode_attn_plan(da.make_shape(tiles=dict(step_mode=4), **pages)).fused == 1
+    tiny_shape = dict(batch=1, num_q_heads=4, num_kv_heads=1, max_seq_len=256, hidden=512)
+    assert da.decode_attn_plan(da.make_shape(**tiny_shape)).fused == 3
+    assert da.decode_attn_plan(da.make_shape(tiles=dict(step_mode=1), **tiny_shape)).fused == 1
+    assert da.decode_attn_plan(da.make_shape(tiles=dict(step_mode=2), **tiny_shape)).fused == 0
 
 
 def _table_rows():

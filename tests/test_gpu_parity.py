@@ -256,8 +256,10 @@ FUSED = [
 
 @pytest.mark.parametrize("case", FUSED, ids=lambda c: "B%d_H%d_KV%d_Lmax%d_N%d" % (c[0], c[1], c[2], c[4], c[5]))
 def test_single_launch_step_matches_the_oracle_and_two_launches(gpu, case):
+    # (step_mode 1: the small single-launch step also where the tiny step would be the built-in)
     B, Hq, Hkv, sl, Lmax, hidden = case
-    assert da.decode_attn_plan(da.make_shape(B, Hq, Hkv, Lmax, hidden)).fused == 1
+    small = dict(step_mode=1)
+    assert da.decode_attn_plan(da.make_shape(B, Hq, Hkv, Lmax, hidden, tiles=small)).fused == 1
     inp = workloads.custom_decode_inputs(B, Hq, Hkv, sl, max_seq_len=Lmax, hidden=hidden, seed=B * 1000 + Hq + hidden)
     q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
     s, w = dev_i32(inp["seq_lens"]), dev_bf16(inp["o_weight"])
@@ -265,7 +267,8 @@ def test_single_launch_step_matches_the_oracle_and_two_launches(gpu, case):
     flat = host_words(da.decode_attn_only(q, k, v, s, workspace=ws))
     outs = []
     for separate in (False, True, False, False):
-        outs.append(host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, separate=separate)))
+        outs.append(host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, separate=separate,
+                                                  tiles=None if separate else small)))
         _status_ok(ws, "single launch")
         _counter_block_is_clear(ws)
     _check_step(inp, {"flat": flat, "out": outs[0]}, what="single launch")
@@ -474,6 +477,48 @@ def test_single_launch_step_timeout_is_reported(gpu):
     _status_ok(ws, "after the counters were zero-filled")
     _counter_block_is_clear(ws)
     _check_step(inp, {"flat": flat, "out": out}, what="after a timeout")
+
+
+# ---- the tiny step: every workgroup computes the whole attention ----------------
+
+TINY = [
+    # (batch, Hq, Hkv, seq_lens, max_seq_len, hidden)
+    (1, 4, 1, [256], 256, 512),          # the tiny workload's shape
+    (2, 16, 2, [128, 5], 128, 256),      # two sequences per kv head, 256 KiB of K/V
+    (1, 16, 1, [200], 200, 264),         # group 16; a last column tile half past N
+    (2, 4, 1, [1, 250], 250, 512),       # a single key (its output is the value row) and a ragged tail
+    (1, 8, 8, [33], 40, 1040),           # eight kv heads of one query head each
+]
+
+
+@pytest.mark.parametrize("case", TINY, ids=lambda c: "B%d_H%d_KV%d_Lmax%d_N%d" % (c[0], c[1], c[2], c[4], c[5]))
+def test_tiny_step_matches_the_oracle(gpu, case):
+    B, Hq, Hkv, sl, Lmax, hidden = case
+    tiles = dict(step_mode=4)
+    assert da.decode_attn_plan(da.make_shape(B, Hq, Hkv, Lmax, hidden, tiles=tiles)).fused == 3
+    inp = workloads.custom_decode_inputs(B, Hq, Hkv, sl, max_seq_len=Lmax, hidden=hidden, seed=B * 31 + Hq + hidden)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    s, w = dev_i32(inp["seq_lens"]), dev_bf16(inp["o_weight"])
+    ws = PoisonedWorkspace()
+    flat = host_words(da.decode_attn_only(q, k, v, s, workspace=ws))
+    out = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, tiles=tiles))
+    _status_ok(ws, "tiny step")
+    _check_step(inp, {"flat": flat, "out": out}, what="tiny step")
+    again = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=ws, tiles=tiles))
+    np.testing.assert_array_equal(out, again)
+
+
+def test_tiny_step_single_key_projects_the_value_rows(gpu):
+    # one key per sequence: the attention output is that key's value row exactly, so the step's
+    # output is the oracle's projection of the value rows
+    B, Hq, Hkv, hidden = 2, 8, 2, 256
+    inp = workloads.custom_decode_inputs(B, Hq, Hkv, [1, 1], max_seq_len=3, hidden=hidden, seed=43)
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    s, w = dev_i32(inp["seq_lens"]), dev_bf16(inp["o_weight"])
+    out = host_words(da.decode_attn_fwd(q, k, v, s, w, workspace=PoisonedWorkspace(), tiles=dict(step_mode=4)))
+    flat = np.stack([np.concatenate([inp["v"][b, qh // (Hq // Hkv), 0] for qh in range(Hq)]) for b in range(B)])
+    _, ref = oracle.oproj(flat, inp["o_weight"])
+    assert_within_fp32_sum_bound(out, ref, flat, inp["o_weight"], "tiny step, one key")
 
 
 # ---- the single-launch large step against two launches -----------------------
