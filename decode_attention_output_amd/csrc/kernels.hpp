@@ -150,6 +150,7 @@ struct StepTinyParams {
   uint16_t* out;            // bf16 [B, N]
   int B, Hq, Hkv, G, Lmax, N;
   float scale_log2;         // softmax scale * log2(e)
+  int xcds, per_xcd;        // set by the launch: column tiles on the first xcds XCDs, per_xcd each
 };
 constexpr int kTinyCols = 16;                    // output columns per workgroup
 constexpr int kTinyMaxK = 2048;                  // Hq * 128 at most

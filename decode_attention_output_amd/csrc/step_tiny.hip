@@ -8,7 +8,7 @@
 // reads are served by L2) instead of waiting for attention workgroups: every
 // cross-workgroup hand-over costs a device-coherent store, an atomic and a
 // load, about a microsecond each, which is most of such a step. A workgroup
-// owns kTinyCols output columns over all of K:
+// owns kTinyCols output columns over all of K (placement: see kTinyXcds):
 //  1. it requests its weight tile at once (thread t holds rows t, t + 256, ...,
 //     32 bytes each), so the weight streams while the attention runs;
 //  2. for every (batch, kv head) sequence, its four waves take interleaved
@@ -23,6 +23,14 @@ namespace da {
 
 namespace {
 
+// Workgroup i of a launch runs on XCD i % 8, and the XCDs begin a launch one
+// after another (the last ~2-4 us after the first). The column tiles therefore
+// go to the first kTinyXcds XCDs, more only where they would not fit one per
+// compute unit; the other workgroups exit at once. Measured on the 4/1-head,
+// 256-key, 512-column step: 2 XCDs 8.1-8.2 us, 1 XCD or all 8 8.3 us.
+constexpr int kTinyXcds = 2;
+constexpr int kXcds = 8;
+constexpr int kCusPerXcd = 32;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kRowsPerThread = kTinyMaxK / kThreads;
@@ -45,7 +53,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_tiny_kernel(StepTinyP
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int col = lane & 15, grp = lane >> 4;
   const int B = p.B, G = p.G, K = p.Hq * kHeadDim;
-  const int n0 = blockIdx.x * kTinyCols;
+  // column tiles xcd * per_xcd + slot: consecutive ones share an XCD's L2
+  const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+  if (xcd >= p.xcds) return;
+  const int n0 = (xcd * p.per_xcd + slot) * kTinyCols;
+  if (n0 >= p.N) return;
   DA_TRACE(0);
 
   // ---- 1. the weight tile: rows t + 256 i, columns n0 .. n0+15 (two 16-byte loads a row) ----
@@ -152,8 +164,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_step_tiny_kernel(StepTinyP
 
 }  // namespace
 
-hipError_t launch_decode_step_tiny(const StepTinyParams& p, int gpad, hipStream_t s) {
-  const dim3 grid((p.N + kTinyCols - 1) / kTinyCols), block(kThreads);
+hipError_t launch_decode_step_tiny(const StepTinyParams& prm, int gpad, hipStream_t s) {
+  // the fewest leading XCDs that hold the column tiles one per compute unit
+  StepTinyParams p = prm;
+  const int tiles = (p.N + kTinyCols - 1) / kTinyCols;
+  p.xcds = kTinyXcds;
+  while (p.xcds < kXcds && (tiles + p.xcds - 1) / p.xcds > kCusPerXcd) p.xcds *= 2;
+  p.per_xcd = (tiles + p.xcds - 1) / p.xcds;
+  const dim3 grid(kXcds * p.per_xcd), block(kThreads);
   switch (gpad) {
     case 1: decode_step_tiny_kernel<1><<<grid, block, 0, s>>>(p); break;
     case 2: decode_step_tiny_kernel<2><<<grid, block, 0, s>>>(p); break;

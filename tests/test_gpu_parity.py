@@ -487,7 +487,8 @@ TINY = [
     (2, 16, 2, [128, 5], 128, 256),      # two sequences per kv head, 256 KiB of K/V
     (1, 16, 1, [200], 200, 264),         # group 16; a last column tile half past N
     (2, 4, 1, [1, 250], 250, 512),       # a single key (its output is the value row) and a ragged tail
-    (1, 8, 8, [33], 40, 1040),           # eight kv heads of one query head each
+    (1, 8, 8, [33], 40, 1040),           # eight kv heads of one query head each; 65 column tiles on 4 XCDs
+    (1, 4, 1, [64], 64, 8200),           # 513 column tiles: all eight XCDs, the last one past N
 ]
 
 
