@@ -78,6 +78,7 @@ __global__ __launch_bounds__(NW * kWave) void gemm_narrow_kernel(GemmParams p) {
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int i = lane & 15, g = lane >> 4;
   char* const stage = s_stage[wave];
+  DA_TRACE(14);
 
   // B from column n0 on (reads past the end return 0; columns past N are never stored)
   const uint32_t rowb = (uint32_t)p.N * 2;
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(NW * kWave) void gemm_narrow_kernel(GemmParams p) {
 #pragma unroll
         for (int c = 0; c < kLoads; ++c) *reinterpret_cast<uint4*>(wp + c * kRowsPerLoad * kRow) = wt[j][c];
         wave_lds_fence();
+        if (s0 + j == 0) DA_TRACE(1);
         const uint4 a = make_uint4(xa[j][0].x, xa[j][0].y, xa[j][1].x, xa[j][1].y);
 #pragma unroll
         for (int jj = 0; jj < NC / 16; ++jj) {
@@ -128,12 +130,14 @@ __global__ __launch_bounds__(NW * kWave) void gemm_narrow_kernel(GemmParams p) {
       }
     }
   }
+  DA_TRACE(2);
   // lane holds C[4g + r][16jj + i]; the waves' sums in wave order
 #pragma unroll
   for (int jj = 0; jj < NC / 16; ++jj)
 #pragma unroll
     for (int r = 0; r < 4; ++r) s_red[wave][4 * g + r][16 * jj + i] = acc[jj][r];
   __syncthreads();
+  DA_TRACE(3);
   if (t >= 16 * NC / kOut) return;
   const int row = t / (NC / kOut), col = (t % (NC / kOut)) * kOut;
   float v[kOut];
@@ -155,6 +159,7 @@ __global__ __launch_bounds__(NW * kWave) void gemm_narrow_kernel(GemmParams p) {
                                                   (uint32_t)to_out<F16>(v[2]) | ((uint32_t)to_out<F16>(v[3]) << 16));
     }
   }
+  DA_TRACE(6);
 }
 
 }  // namespace
