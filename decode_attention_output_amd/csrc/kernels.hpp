@@ -117,6 +117,8 @@ struct GemmWait {
   int waiter;
 };
 
+constexpr int kXcds = 8;  // XCDs of an MI355X; workgroup i of a launch runs on XCD i % kXcds
+
 struct StepParams {
   const uint16_t* q;        // bf16 [B, Hq, 128]
   const uint16_t* k;        // bf16 [B, Hkv, Lmax, 128]

@@ -29,7 +29,6 @@ namespace {
 // compute unit; the other workgroups exit at once. Measured on the 4/1-head,
 // 256-key, 512-column step: 2 XCDs 8.1-8.2 us, 1 XCD or all 8 8.3 us.
 constexpr int kTinyXcds = 2;
-constexpr int kXcds = 8;
 constexpr int kCusPerXcd = 32;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
