@@ -195,8 +195,9 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
   };
 
   // ---- the merge of more partials than one batch holds ----
-  // Every partial's running max and weight sum are read first (one per thread)
-  // and turned into per-query weights in LDS, so that the output loads of all
+  // Every partial's running max and weight sum are read first (one per lane,
+  // a segment of lanes per query that reduces them with shuffles) and turned
+  // into per-query weights in LDS, so that the output loads of all
   // partials can be requested together: two memory trips where batches of
   // kMergeBatch take one trip each. The outputs are then added in partial
   // order, each scaled by its weight (deterministic).
@@ -228,30 +229,53 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
           ov[u][pp] = rsrc_ld16_coherent(part_o, off);
         }
     };
+    // query g's partials in a segment of kSeg lanes (lane j of it: partial j) when they
+    // fit, so that each maximum and weight sum is a few shuffles; else one thread per query
+    constexpr int kSeg = NT / GP < kWave ? NT / GP : kWave;
+    const bool in_seg = P <= kSeg;  // uniform
+    const int sg = t / kSeg, sj = t % kSeg;
+    const bool mine = in_seg ? (sg < G && sj < P) : t < P * G;
     uint2 ml = make_uint2(0u, 0u);
-    if (t < P * G) ml = rsrc_ld8_coherent(part_ml, (uint32_t)(slot0 * G + t) * 8);
+    if (mine) ml = rsrc_ld8_coherent(part_ml, (uint32_t)(in_seg ? (slot0 + sj) * G + sg : slot0 * G + t) * 8);
     load_batch(0);
-    if (t < P * G) {
-      w_f[t] = __builtin_bit_cast(float, ml.x);
-      w_l[t] = __builtin_bit_cast(float, ml.y);
-    }
-    __syncthreads();
-    if (t < G) {
-      float M = -INFINITY;
-#pragma unroll 8
-      for (int j = 0; j < P; ++j) M = fmaxf(M, w_f[j * G + t]);
-      float Ls = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < P; ++j) {
-        const float m = w_f[j * G + t];
-        const float f = m == -INFINITY ? 0.f : exp2f(m - M);  // an empty partial weighs nothing
-        Ls = fmaf(f, w_l[j * G + t], Ls);
-        w_f[j * G + t] = f;
+    if (in_seg) {
+      const float m = mine ? __builtin_bit_cast(float, ml.x) : -INFINITY;
+      float M = m;
+#pragma unroll
+      for (int off = kSeg / 2; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+      const float f = m == -INFINITY ? 0.f : exp2f(m - M);  // an empty partial weighs nothing
+      float Ls = f * (mine ? __builtin_bit_cast(float, ml.y) : 0.f);
+#pragma unroll
+      for (int off = kSeg / 2; off >= 1; off >>= 1) Ls += __shfl_xor(Ls, off);
+      if (mine) w_f[sj * G + sg] = f;
+      if (sg < G && sj == 0) {
+        w_M[sg] = M;
+        w_L[sg] = Ls;
       }
-      w_M[t] = M;
-      w_L[t] = Ls;
+    } else {
+      if (mine) {
+        w_f[t] = __builtin_bit_cast(float, ml.x);
+        w_l[t] = __builtin_bit_cast(float, ml.y);
+      }
+      __syncthreads();
+      if (t < G) {
+        float M = -INFINITY;
+#pragma unroll 8
+        for (int j = 0; j < P; ++j) M = fmaxf(M, w_f[j * G + t]);
+        float Ls = 0.f;
+#pragma unroll 8
+        for (int j = 0; j < P; ++j) {
+          const float m = w_f[j * G + t];
+          const float f = m == -INFINITY ? 0.f : exp2f(m - M);
+          Ls = fmaf(f, w_l[j * G + t], Ls);
+          w_f[j * G + t] = f;
+        }
+        w_M[t] = M;
+        w_L[t] = Ls;
+      }
     }
     __syncthreads();
+    DA_TRACE(5);
     float acc[kPairsPerThread][4];
 #pragma unroll
     for (int pp = 0; pp < kPairsPerThread; ++pp)
@@ -273,6 +297,7 @@ __device__ __forceinline__ void attn_streamk_body(const AttnParams& p, long wg, 
           }
         }
     }
+    DA_TRACE(7);
     auto write_pair = [&](int pr, const float (&o)[4]) {
       const int g = pr / D4, d4 = pr % D4;
       const int qh = h * G + g;
