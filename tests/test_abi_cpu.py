@@ -212,9 +212,11 @@ def test_plan_tiles_follow_the_per_matmul_rules(lib, cfg):
         assert plan.split_len % 32 == 0 and plan.split_len * plan.num_splits >= keys
         assert plan.split_len * (plan.num_splits - 1) < keys + 32 * plan.num_splits
         # the keys are spread over 176 workgroups (22 per XCD, the measured best over a set of
-        # steps) when the problem allows it, but never so many that a workgroup streams fewer
-        # than 128 keys
-        assert plan.qk.workgroups >= min(176, keys // 128)
+        # steps), or the count of the shape's measured table row, when the problem allows it,
+        # but never so many that a workgroup streams fewer than 128 keys
+        row = _table_tiles(cfg)
+        want = row["attn_workgroups"] if row and row["attn_workgroups"] else 176
+        assert plan.qk.workgroups >= min(want, keys // 128)
         assert plan.split_len >= min(128, 32 * (-(-keys // 32)))
         assert plan.oproj.workgroups >= min(256, (cfg["hidden"] // 128) * (cfg["num_q_heads"] * 128 // 128))
     # projection path: the single-launch small and tiny steps' own VALU projections, else the MFMA
@@ -325,6 +327,18 @@ def _table_rows():
             if line.startswith("TILE_ENTRY("):
                 rows.append([int(v) for v in line[len("TILE_ENTRY("):line.index(")")].split(",")])
     return rows
+
+
+def _table_tiles(cfg):
+    """The tiles of the table row of a shape (head_dim 128 unless given), or None."""
+    from decode_attention_output_amd import autotune
+
+    key = (cfg["batch"], cfg["num_q_heads"], cfg["num_kv_heads"], cfg.get("head_dim", 128), cfg["max_seq_len"],
+           cfg["hidden"])
+    for row in _table_rows():
+        if tuple(row[:6]) == key:
+            return dict(zip(autotune.TILE_FIELDS, row[6:]))
+    return None
 
 
 def test_measured_tile_table_rows_are_valid_and_used(lib):
