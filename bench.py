@@ -542,8 +542,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on exactly one GPU; --gpus %d (WORLD_SIZE %d) is not supported. "
-              "Multi-GPU sharding is described in DESIGN.md, not run." % (args.gpus, world), file=sys.stderr)
+        print("bench.py: the decode step runs on exactly one GPU; --gpus %d (WORLD_SIZE %d) is not supported "
+              "(sharding across GPUs is not implemented)." % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
